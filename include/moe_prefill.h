@@ -1,0 +1,181 @@
+/*
+ * moe_prefill.h -- C ABI of libmoe_prefill.so, the MI355X (gfx950) prompt-path MoE expert layer.
+ *
+ * The layer is the one the Strata prompt-path pages tune:
+ *   [G1] "#439 prefill: a group's expert gathers in one launch (bit-identical, long prompts +4%)"
+ *   [G2] "Prompt path: an MMQ group's experts gathered in one launch, after one wait, released by
+ *         one event (-9% on a 32K prompt, same output)"
+ *   [QS] "#1368 prefill: quantize each token's MoE input once and scatter it to its k rows
+ *         (the same bytes)"
+ *   [CS] "#1282 prefill: STRATA_PREFILL_CPU_SHARE=auto hands a small chunk's least-routed experts
+ *         to the idle CPU pool (opt-in)"
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every buffer; the
+ *     library allocates nothing on any compute path and keeps no state between calls (the
+ *     optional stage profiler aside).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is enqueued on it
+ *     and the call returns at once; nothing synchronises with the host.
+ *   - Return value: MOE_OK (0) or a negative moe_status.  Argument checks run on the host before
+ *     anything is enqueued (MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE); a failed launch returns
+ *     MOE_EHIP.  Device-side preconditions (0 <= expert id < E, finite inputs) are the caller's:
+ *     the kernels never read or write out of bounds when they are broken, but the results are then
+ *     unspecified.
+ *   - Calls are reentrant; calls that share output or workspace buffers must not overlap.
+ *
+ * Byte formats (little endian)
+ *   Q8_0 weight block, 34 B : fp16 d | int8 q[32]                          w_j = d*q_j
+ *   Q4_1 weight block, 20 B : fp16 d | fp16 m | u8 qs[16]                  w_j = d*q_j + m
+ *                             qs[j]: element j in the low nibble, element j+16 in the high nibble
+ *   expert, expert_bytes    : gate [F rows x H/32 blocks] | up [F x H/32] | down [H x F/32],
+ *                             each matrix row-major with its blocks along the reduction dimension
+ *   q8_1 row of n values    : n/128 groups of 144 B: (fp16 d, fp16 s) of its 4 blocks of 32, then
+ *                             the 4 blocks' int8 q.  d = amax/127 (fp32), q = roundf(v/d), s = d*sum q
+ *                             ([QS] opening section and "Identity": the DS4 layout, which carries the
+ *                             s that Q4_1's min term needs).
+ */
+#ifndef MOE_PREFILL_H
+#define MOE_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_GROUP 16     /* experts per group buffer ([G1] "What": MMQ_GROUP = 16) */
+#define MOE_MAX_E 2048       /* largest expert count the kernels accept */
+#define MOE_MAX_K 64         /* largest routes per token */
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* a null pointer, a size out of range, inconsistent arguments */
+    MOE_EUNSUPPORTED = -2,  /* a valid request this build does not implement (H or F not a
+                               multiple of 128, E > MOE_MAX_E, K > MOE_MAX_K, unknown type) */
+    MOE_EWORKSPACE = -3,    /* the workspace is smaller than the matching *_workspace_size() */
+    MOE_EHIP = -4           /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_Q8_0 = 0, MOE_Q4_1 = 1 } moe_wtype;
+
+typedef enum {
+    MOE_EPI_F32 = 0,           /* out = fp32 [rows x n_out] products (the down projection) */
+    MOE_EPI_SWIGLU_Q8_1 = 1,   /* out = q8_1 rows of h = silu(gate)*up, [rows x n_out/128*144] */
+    MOE_EPI_I32_BLOCKDOTS = 2  /* out = int32 [rows x n_out x k_in/32] raw block dots (checking) */
+} moe_epilogue;
+
+int moe_abi_version(void);
+const char *moe_strerror(int status);
+
+/* Sizes (bytes). */
+size_t moe_block_bytes(int wtype);                      /* 34 or 20; 0 if unknown */
+size_t moe_expert_bytes(int H, int F, int wtype);       /* 3*H*F/32 blocks */
+size_t moe_q8_1_row_bytes(int n);                       /* n/128*144 */
+size_t moe_build_maps_workspace_size(int T, int K, int E);
+size_t moe_workspace_size(int T, int H, int F, int E, int K, int wtype, int group_size);
+
+/* a0  Top-K routing ([QS] "Identity": routing built as Prefill builds it, 10 of 512 experts).
+ * logits fp32 [T x E] -> idx int32 [T x K] (the K largest logits, equal logits: lower id first),
+ * w fp32 [T x K] (softmax over the K chosen logits = softmax, top-K, renormalise).  E <= 2048. */
+int moe_route_topk(const float *logits, int T, int E, int K, int32_t *idx, float *w,
+                   void *stream);
+
+/* a1  Token -> row maps ([QS] opening section: src_dev names each row's source; token t's k-th row
+ * is slot[t*K+k], the inverse of src_dev).  From idx int32 [T x K]:
+ *   counts [E]; offsets [E+1] (exclusive prefix of counts); src [T*K]: row r -> t*K+k, rows grouped
+ *   by expert id ascending, ascending t*K+k inside an expert (stable); slot [T*K] = src^-1;
+ *   order [E]: the experts with rows, in ring order from ring_start ([G2] "What changes": skipped
+ *   ring entries hold no rows); n_active [1]: how many.  Group g of size gs is order[gs*g ...].
+ * ws: at least moe_build_maps_workspace_size(T, K, E) bytes of device scratch. */
+int moe_build_maps(const int32_t *topk_idx, int T, int K, int E, int ring_start,
+                   int32_t *counts, int32_t *offsets, int32_t *src, int32_t *slot,
+                   int32_t *order, int32_t *n_active, void *ws, size_t ws_bytes, void *stream);
+
+/* a2  q8_1 quantisation of the layer input ([QS] opening section).
+ * x fp32 [T x H] row-major; q8 [T*K x moe_q8_1_row_bytes(H)].
+ * mode 0 (scatter): each token row is read once and written to rows slot[t*K+k], k < K.
+ * mode 1 (per-row gather, the form the page replaces): row r quantises token src[r]/K.
+ * Both write the same bytes. */
+int moe_quantize_scatter_q8_1(const float *x, int T, int H, int K, const int32_t *slot,
+                              const int32_t *src, int mode, void *q8, void *stream);
+
+/* a3  One group's gather in one launch ([G1] "What", [G2] "What changes"; blockIdx.y = expert).
+ * src_ptrs [host]: n (1..16) device pointers to experts of expert_bytes each.  Expert j lands at
+ * group_buf + (first_pos + j) * pos_stride, first_pos + n <= 16 (a batch may start mid-group).
+ * The bytes are exactly those of one copy per expert; pointers or sizes that are not 16-byte
+ * multiples take a byte-wise path instead of 16-byte copies. */
+int moe_gather_group(const void *const *src_ptrs, int n, size_t expert_bytes, void *group_buf,
+                     int first_pos, size_t pos_stride, void *stream);
+
+/* a4..a6  Grouped quantised matmul (MMQ) over one group buffer ([G2] "What changes", [QS] opening
+ * section).  Position j < n_group of group_buf (at j*pos_stride) holds expert group_experts[j]
+ * ([host] array, each in [0, E)); its rows are offsets[e] .. offsets[e+1]-1 (offsets: int32 [E+1],
+ * device) of act_q8 (q8_1 rows of k_in values,
+ * grouped by expert as moe_build_maps orders them).  The weight matrix starts mat_offset bytes into
+ * each expert and has n_out rows of k_in/32 blocks (for MOE_EPI_SWIGLU_Q8_1: gate = rows 0..n_out-1,
+ * up = rows n_out..2*n_out-1).  Per block b: I_b = integer dot of the 32 int8 (Q8_0) or 4-bit (Q4_1)
+ * weights with the 32 int8 activations; y_b = dw*dx*I_b (+ mw*sx for Q4_1); a row's result is the
+ * sum over b.  Output row r is written at row r of `out` (rows of other experts untouched):
+ *   MOE_EPI_F32:           fp32 [* x n_out]
+ *   MOE_EPI_SWIGLU_Q8_1:   q8_1 rows of h = silu(g)*u (n_out values); debug_h, if not NULL, gets the
+ *                          fp32 h [* x n_out] that was quantised
+ *   MOE_EPI_I32_BLOCKDOTS: int32 [* x n_out x k_in/32], the raw I_b
+ * n_out and k_in: multiples of 128.  group_buf, pos_stride and mat_offset: multiples of 4 bytes;
+ * act_q8: 16-byte aligned.  The matrix must lie inside each position's bytes (caller's duty). */
+int moe_mmq_grouped(int wtype, const void *group_buf, size_t pos_stride, size_t mat_offset,
+                    int n_out, int k_in, const int32_t *group_experts, int n_group,
+                    const int32_t *offsets, int E, const void *act_q8, int epilogue, void *out,
+                    float *debug_h, void *stream);
+
+/* a7  Combine ([CS] "What it does": the expert rows in Dm are unweighted; the combine weights them).
+ * out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i], k ascending; Dm fp32 [T*K x H]. */
+int moe_combine(const float *Dm, const int32_t *slot, const float *topk_w, int T, int K, int H,
+                float *out, void *stream);
+
+/* a1..a7  The whole layer: maps, quantise-scatter, every group's gather, MMQ gate/up with SwiGLU and
+ * q8_1 requantisation, MMQ down into Dm, combine.
+ * x fp32 [T x H]; topk_idx int32 / topk_w fp32 [T x K]; pool: the experts, expert e at byte
+ * expert_off[e] (int64 [E], device) of expert_bytes = moe_expert_bytes(H, F, wtype).
+ * group_size (1..16) and ring_start (0..E-1) set which experts share a group buffer; the output is
+ * bit-identical for every choice ([G1] "What": the same bytes land in the same places; [G2] "What
+ * changes": the products and their order are unchanged).  ws: moe_workspace_size(...) bytes.
+ * out fp32 [T x H].  H, F multiples of 128; E <= 2048; K <= min(E, 64). */
+int moe_prefill_layer(const float *x, int T, int H, int F, int E, int K,
+                      const int32_t *topk_idx, const float *topk_w, int wtype,
+                      const void *pool, const int64_t *expert_off, size_t expert_bytes,
+                      int group_size, int ring_start, void *ws, size_t ws_bytes, float *out,
+                      void *stream);
+
+/* Where moe_prefill_layer keeps its intermediate results inside ws, for checking them:
+ * the byte offset of region `which` (MOE_WS_*) for these arguments, or (size_t)-1. */
+enum {
+    MOE_WS_COUNTS = 0,   /* int32 [E] */
+    MOE_WS_OFFSETS = 1,  /* int32 [E+1] */
+    MOE_WS_SRC = 2,      /* int32 [T*K] */
+    MOE_WS_SLOT = 3,     /* int32 [T*K] */
+    MOE_WS_ORDER = 4,    /* int32 [E], then n_active at MOE_WS_NACTIVE */
+    MOE_WS_NACTIVE = 5,  /* int32 [1] */
+    MOE_WS_Q8X = 6,      /* q8_1 rows of x [T*K x moe_q8_1_row_bytes(H)] */
+    MOE_WS_GROUPS = 7,   /* group buffers: active expert i (ring order) at i * stride */
+    MOE_WS_HQ8 = 8,      /* q8_1 rows of h [T*K x moe_q8_1_row_bytes(F)] */
+    MOE_WS_DM = 9,       /* fp32 [T*K x H] */
+    MOE_WS_GROUP_STRIDE = 10  /* not an offset: the byte stride between group positions */
+};
+size_t moe_workspace_offset(int which, int T, int H, int F, int E, int K, int wtype,
+                            int group_size);
+
+/* Optional stage timing of moe_prefill_layer with HIP events recorded on the call's stream.
+ * moe_profile_begin(n) arms it for the next n calls (creates the events); moe_profile_end()
+ * waits for the last recorded event, writes ms [n_done x MOE_N_STAGES] (stage order: maps,
+ * quantize, gather, gate/up, down, combine) into ms [host] (capacity max_calls rows), returns
+ * the number of calls recorded (or a negative status) and disarms it. */
+#define MOE_N_STAGES 6
+int moe_profile_begin(int n_calls);
+int moe_profile_end(float *ms, int max_calls);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -61,6 +61,7 @@ def lib():
             "orc_block_idot": (ctypes.c_int32, [i, P, P]),
             "orc_row_dot": (ctypes.c_double, [i, P, P, i]),
             "orc_block_dots": (None, [i, P, i, i, P, i, P]),
+            "orc_mmq_rows": (None, [i, P, i, i, P, i, P]),
             "orc_expert_row": (None, [i, P, i, i, P, P, P, P]),
             "orc_combine": (None, [P, P, P, i, i, i, P]),
             "orc_prefill_layer": (i, [P, i, i, i, i, i, P, P, i, P, P, P, P, P, P, P]),
@@ -212,6 +213,16 @@ def block_dots(wtype: int, wmat, n_out: int, k_in: int, act_q8):
     n_rows = act_q8.shape[0]
     out = np.empty((n_rows, n_out, k_in // 32), np.int32)
     lib().orc_block_dots(wtype, _p(wmat), n_out, k_in, _p(act_q8), n_rows, _p(out))
+    return out
+
+
+def mmq_rows(wtype: int, wmat, n_out: int, k_in: int, act_q8):
+    """fp64 products [n_rows x n_out] of activation rows with a weight matrix's rows."""
+    wmat = _c(wmat, np.uint8)
+    act_q8 = _c(act_q8, np.uint8)
+    n_rows = act_q8.shape[0]
+    out = np.empty((n_rows, n_out), np.float64)
+    lib().orc_mmq_rows(wtype, _p(wmat), n_out, k_in, _p(act_q8), n_rows, _p(out))
     return out
 
 

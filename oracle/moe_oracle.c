@@ -312,6 +312,19 @@ void orc_block_dots(int wtype, const uint8_t *wmat, int n_out, int k_in,
             }
 }
 
+/* Products of n_rows activation rows with every row of one weight matrix (fp64):
+ * out[r*n_out + n] = orc_row_dot(row n of wmat, activation row r). */
+void orc_mmq_rows(int wtype, const uint8_t *wmat, int n_out, int k_in, const uint8_t *act_q8,
+                  int n_rows, double *out)
+{
+    size_t wrb = (size_t)(k_in / 32) * orc_block_bytes(wtype), arb = orc_q8_1_row_bytes(k_in);
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < n_rows; ++r)
+        for (int n = 0; n < n_out; ++n)
+            out[(size_t)r * n_out + n] =
+                orc_row_dot(wtype, wmat + (size_t)n * wrb, act_q8 + (size_t)r * arb, k_in);
+}
+
 /* ---------------------------------------------------------------------------------------
  * a4..a6  one routed row through one expert.  [QS] opening section: the down-projection
  * input is quantised to q8_1 again ("the down-projection quantizations").  The pages do not

@@ -76,6 +76,8 @@ int32_t orc_block_idot(int wtype, const uint8_t *wblock, const int8_t *xq);
 double  orc_row_dot(int wtype, const uint8_t *wrow, const uint8_t *xrow_q8, int k_in);
 void    orc_block_dots(int wtype, const uint8_t *wmat, int n_out, int k_in,
                        const uint8_t *act_q8, int n_rows, int32_t *out);
+void    orc_mmq_rows(int wtype, const uint8_t *wmat, int n_out, int k_in,
+                     const uint8_t *act_q8, int n_rows, double *out);
 
 /* --- a4..a6 one routed row through one expert ------------------------------------------ */
 void orc_expert_row(int wtype, const uint8_t *expert, int H, int F, const uint8_t *xrow_q8,

@@ -1,0 +1,208 @@
+"""Thin Python binding of libmoe_prefill.so (include/moe_prefill.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.  Tensors are torch
+tensors on the GPU; the stream defaults to torch's current stream.  Loading fails loudly when the
+library has not been built (``python -m quantized_expert_grouped_amd.build``) -- there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_prefill.so")
+
+Q8_0, Q4_1 = 0, 1
+EPI_F32, EPI_SWIGLU_Q8_1, EPI_I32_BLOCKDOTS = 0, 1, 2
+WS_COUNTS, WS_OFFSETS, WS_SRC, WS_SLOT, WS_ORDER, WS_NACTIVE, WS_Q8X, WS_GROUPS, WS_HQ8, WS_DM, \
+    WS_GROUP_STRIDE = range(11)
+N_STAGES = 6
+STAGES = ("maps", "quantize", "gather", "gate_up", "down", "combine")
+
+STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EWORKSPACE",
+          -4: "MOE_EHIP"}
+
+# name -> (restype, argtypes); the order of this table is the header's order
+P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "moe_abi_version": (I, []),
+    "moe_strerror": (ctypes.c_char_p, [I]),
+    "moe_block_bytes": (SZ, [I]),
+    "moe_expert_bytes": (SZ, [I, I, I]),
+    "moe_q8_1_row_bytes": (SZ, [I]),
+    "moe_build_maps_workspace_size": (SZ, [I, I, I]),
+    "moe_workspace_size": (SZ, [I, I, I, I, I, I, I]),
+    "moe_route_topk": (I, [P, I, I, I, P, P, P]),
+    "moe_build_maps": (I, [P, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
+    "moe_quantize_scatter_q8_1": (I, [P, I, I, I, P, P, I, P, P]),
+    "moe_gather_group": (I, [P, I, SZ, P, I, SZ, P]),
+    "moe_mmq_grouped": (I, [I, P, SZ, SZ, I, I, P, I, P, I, P, I, P, P, P]),
+    "moe_combine": (I, [P, P, P, I, I, I, P, P]),
+    "moe_prefill_layer": (I, [P, I, I, I, I, I, P, P, I, P, P, SZ, I, I, P, SZ, P, P]),
+    "moe_workspace_offset": (SZ, [I, I, I, I, I, I, I, I]),
+    "moe_profile_begin": (I, [I]),
+    "moe_profile_end": (I, [P, I]),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status} ({STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m quantized_expert_grouped_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != 0:
+        raise MoeError(name, rc)
+
+
+# ---- sizes ----------------------------------------------------------------------------------
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(status).decode()
+
+
+def block_bytes(wtype: int) -> int:
+    return lib().moe_block_bytes(wtype)
+
+
+def expert_bytes(H: int, F: int, wtype: int) -> int:
+    return lib().moe_expert_bytes(H, F, wtype)
+
+
+def q8_1_row_bytes(n: int) -> int:
+    return lib().moe_q8_1_row_bytes(n)
+
+
+def build_maps_workspace_size(T: int, K: int, E: int) -> int:
+    return lib().moe_build_maps_workspace_size(T, K, E)
+
+
+def workspace_size(T, H, F, E, K, wtype, group_size=16) -> int:
+    return lib().moe_workspace_size(T, H, F, E, K, wtype, group_size)
+
+
+def workspace_offset(which, T, H, F, E, K, wtype, group_size=16) -> int:
+    return lib().moe_workspace_offset(which, T, H, F, E, K, wtype, group_size)
+
+
+# ---- entry points (raise MoeError on a non-zero status; `raw_*` return the status) -------------
+def route_topk(logits, K, idx, w, stream=None):
+    T, E = logits.shape
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), T, E, K, _ptr(idx), _ptr(w),
+                                                  _stream(stream)))
+
+
+def build_maps(topk_idx, E, ring_start, counts, offsets, src, slot, order, n_active, ws,
+               stream=None):
+    T, K = topk_idx.shape
+    _check("moe_build_maps", lib().moe_build_maps(
+        _ptr(topk_idx), T, K, E, ring_start, _ptr(counts), _ptr(offsets), _ptr(src), _ptr(slot),
+        _ptr(order), _ptr(n_active), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def quantize_scatter_q8_1(x, K, slot, src, mode, q8, stream=None):
+    T, H = x.shape
+    _check("moe_quantize_scatter_q8_1", lib().moe_quantize_scatter_q8_1(
+        _ptr(x), T, H, K, _ptr(slot), _ptr(src), mode, _ptr(q8), _stream(stream)))
+
+
+def raw_gather_group(src_ptrs, expert_bytes_, group_buf, first_pos, pos_stride, stream=None):
+    n = len(src_ptrs)
+    arr = (ctypes.c_void_p * max(n, 1))(*[int(p) for p in src_ptrs])
+    return lib().moe_gather_group(ctypes.cast(arr, ctypes.c_void_p) if n else None, n,
+                                  expert_bytes_, _ptr(group_buf), first_pos, pos_stride,
+                                  _stream(stream))
+
+
+def gather_group(src_ptrs, expert_bytes_, group_buf, first_pos, pos_stride, stream=None):
+    _check("moe_gather_group", raw_gather_group(src_ptrs, expert_bytes_, group_buf, first_pos,
+                                                pos_stride, stream))
+
+
+def raw_mmq_grouped(wtype, group_buf, pos_stride, mat_offset, n_out, k_in, group_experts,
+                    offsets, E, act_q8, epilogue, out, debug_h=None, stream=None):
+    ge = np.ascontiguousarray(group_experts, dtype=np.int32)
+    return lib().moe_mmq_grouped(
+        wtype, _ptr(group_buf), pos_stride, mat_offset, n_out, k_in,
+        ge.ctypes.data_as(ctypes.c_void_p), len(ge), _ptr(offsets), E, _ptr(act_q8), epilogue,
+        _ptr(out), _ptr(debug_h), _stream(stream))
+
+
+def mmq_grouped(*args, **kw):
+    _check("moe_mmq_grouped", raw_mmq_grouped(*args, **kw))
+
+
+def combine(Dm, slot, topk_w, out, stream=None):
+    T, K = topk_w.shape
+    H = Dm.shape[1]
+    _check("moe_combine", lib().moe_combine(_ptr(Dm), _ptr(slot), _ptr(topk_w), T, K, H,
+                                            _ptr(out), _stream(stream)))
+
+
+def raw_prefill_layer(x, topk_idx, topk_w, wtype, pool, expert_off, F, E, group_size, ring_start,
+                      ws, out, stream=None, ws_bytes=None):
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    eb = expert_bytes(H, F, wtype)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    return lib().moe_prefill_layer(_ptr(x), T, H, F, E, K, _ptr(topk_idx), _ptr(topk_w), wtype,
+                                   _ptr(pool), _ptr(expert_off), eb, group_size, ring_start,
+                                   _ptr(ws), nbytes, _ptr(out), _stream(stream))
+
+
+def prefill_layer(*args, **kw):
+    _check("moe_prefill_layer", raw_prefill_layer(*args, **kw))
+
+
+def profile_begin(n_calls: int) -> None:
+    _check("moe_profile_begin", lib().moe_profile_begin(n_calls))
+
+
+def profile_end(max_calls: int) -> np.ndarray:
+    ms = np.zeros((max_calls, N_STAGES), np.float32)
+    n = lib().moe_profile_end(ms.ctypes.data_as(ctypes.c_void_p), max_calls)
+    if n < 0:
+        raise MoeError("moe_profile_end", n)
+    return ms[:n]

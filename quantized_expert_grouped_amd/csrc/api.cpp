@@ -1,0 +1,333 @@
+// C ABI of libmoe_prefill.so: argument checks, the layer's workspace layout and its launch
+// schedule.  Every compute step runs in the gfx950 kernels of this directory; nothing here
+// computes on the host or synchronises with the device (the opt-in stage profiler aside).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "internal.hpp"
+#include "moe_prefill.h"
+
+namespace {
+
+using namespace moe;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+bool valid_wtype(int wt) { return wt == MOE_Q8_0 || wt == MOE_Q4_1; }
+
+// Region offsets of the layer's workspace (each 256-byte aligned).
+struct Layout {
+  size_t hist, counts, offsets, src, slot, order, nactive, ntiles, tiles, q8x, groups, hq8, dm;
+  size_t group_stride, total;
+  int max_tiles;
+};
+
+bool make_layout(int T, int H, int F, int E, int K, int wt, Layout* L) {
+  if (T < 1 || K < 1 || E < 1 || H < 128 || F < 128 || !valid_wtype(wt)) return false;
+  const size_t R = (size_t)T * K;
+  const size_t eb = moe_expert_bytes(H, F, wt);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L->hist = take((size_t)map_chunks((int)R) * E * 4);
+  L->counts = take((size_t)E * 4);
+  L->offsets = take((size_t)(E + 1) * 4);
+  L->src = take(R * 4);
+  L->slot = take(R * 4);
+  L->order = take((size_t)E * 4);
+  L->nactive = take(4);
+  L->ntiles = take(4);
+  L->max_tiles = max_mtiles((int)R, E, kMmqRows);
+  L->tiles = take((size_t)L->max_tiles * sizeof(MTile));
+  L->q8x = take(R * moe_q8_1_row_bytes(H));
+  L->group_stride = align_up(eb, 256);
+  L->groups = take((size_t)E * L->group_stride);
+  L->hq8 = take(R * moe_q8_1_row_bytes(F));
+  L->dm = take(R * (size_t)H * 4);
+  L->total = o;
+  return true;
+}
+
+// ---- opt-in stage profiler -------------------------------------------------------------------
+constexpr int kEvPerCall = MOE_N_STAGES + 1;
+std::mutex g_prof_mu;
+std::vector<hipEvent_t> g_prof_ev;
+int g_prof_calls = 0;
+int g_prof_done = 0;
+
+void destroy_events() {
+  for (hipEvent_t e : g_prof_ev) (void)hipEventDestroy(e);
+  g_prof_ev.clear();
+  g_prof_calls = g_prof_done = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or type";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_block_bytes(int wtype) {
+  return wtype == MOE_Q8_0 ? 34 : wtype == MOE_Q4_1 ? 20 : 0;
+}
+
+size_t moe_expert_bytes(int H, int F, int wtype) {
+  if (H < 32 || F < 32 || !valid_wtype(wtype)) return 0;
+  return ((size_t)2 * F * (H / 32) + (size_t)H * (F / 32)) * moe_block_bytes(wtype);
+}
+
+size_t moe_q8_1_row_bytes(int n) { return n > 0 ? (size_t)(n / 128) * 144 : 0; }
+
+size_t moe_build_maps_workspace_size(int T, int K, int E) {
+  if (T < 1 || K < 1 || E < 1) return 0;
+  return align_up((size_t)map_chunks(T * K) * E * 4, 256);
+}
+
+size_t moe_workspace_size(int T, int H, int F, int E, int K, int wtype, int group_size) {
+  Layout L;
+  if (group_size < 1 || group_size > MOE_MAX_GROUP) return 0;
+  if (!make_layout(T, H, F, E, K, wtype, &L)) return 0;
+  return L.total;
+}
+
+size_t moe_workspace_offset(int which, int T, int H, int F, int E, int K, int wtype,
+                            int group_size) {
+  Layout L;
+  if (group_size < 1 || group_size > MOE_MAX_GROUP || !make_layout(T, H, F, E, K, wtype, &L))
+    return (size_t)-1;
+  switch (which) {
+    case MOE_WS_COUNTS: return L.counts;
+    case MOE_WS_OFFSETS: return L.offsets;
+    case MOE_WS_SRC: return L.src;
+    case MOE_WS_SLOT: return L.slot;
+    case MOE_WS_ORDER: return L.order;
+    case MOE_WS_NACTIVE: return L.nactive;
+    case MOE_WS_Q8X: return L.q8x;
+    case MOE_WS_GROUPS: return L.groups;
+    case MOE_WS_HQ8: return L.hq8;
+    case MOE_WS_DM: return L.dm;
+    case MOE_WS_GROUP_STRIDE: return L.group_stride;
+    default: return (size_t)-1;
+  }
+}
+
+int moe_route_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w,
+                   void* stream) {
+  if (!logits || !idx || !w || T < 1 || E < 1 || K < 1 || K > E) return MOE_EINVAL;
+  if (E > MOE_MAX_E || K > MOE_MAX_K) return MOE_EUNSUPPORTED;
+  return status_of(launch_route_topk(logits, T, E, K, idx, w, as_stream(stream)));
+}
+
+int moe_build_maps(const int32_t* topk_idx, int T, int K, int E, int ring_start, int32_t* counts,
+                   int32_t* offsets, int32_t* src, int32_t* slot, int32_t* order,
+                   int32_t* n_active, void* ws, size_t ws_bytes, void* stream) {
+  if (!topk_idx || !counts || !offsets || !src || !slot || !order || !n_active || !ws)
+    return MOE_EINVAL;
+  if (T < 1 || K < 1 || E < 1 || K > E || ring_start < 0 || ring_start >= E) return MOE_EINVAL;
+  if ((long long)T * K > (1LL << 30)) return MOE_EUNSUPPORTED;
+  if (E > MOE_MAX_E) return MOE_EUNSUPPORTED;
+  if (ws_bytes < moe_build_maps_workspace_size(T, K, E)) return MOE_EWORKSPACE;
+  MapsOut o{counts, offsets, src, slot, order, n_active, static_cast<int32_t*>(ws),
+            nullptr, nullptr, kMmqRows};
+  return status_of(launch_build_maps(topk_idx, T, K, E, ring_start, o, as_stream(stream)));
+}
+
+int moe_quantize_scatter_q8_1(const float* x, int T, int H, int K, const int32_t* slot,
+                              const int32_t* src, int mode, void* q8, void* stream) {
+  if (!x || !q8 || T < 1 || K < 1 || (mode != 0 && mode != 1)) return MOE_EINVAL;
+  if ((mode == 0 && !slot) || (mode == 1 && !src)) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(q8, 16)) return MOE_EINVAL;
+  if (H < 128 || H % 128 != 0 || K > MOE_MAX_K) return MOE_EUNSUPPORTED;
+  if ((long long)T * K > (1LL << 30)) return MOE_EUNSUPPORTED;
+  return status_of(launch_quantize(x, T, H, K, slot, src, mode, static_cast<uint8_t*>(q8),
+                                   as_stream(stream)));
+}
+
+int moe_gather_group(const void* const* src_ptrs, int n, size_t expert_bytes, void* group_buf,
+                     int first_pos, size_t pos_stride, void* stream) {
+  if (!src_ptrs || !group_buf || n < 1 || n > MOE_MAX_GROUP || first_pos < 0 ||
+      first_pos + n > MOE_MAX_GROUP || expert_bytes == 0)
+    return MOE_EINVAL;
+  if (n > 1 && pos_stride < expert_bytes) return MOE_EINVAL;
+  GatherPtrs p{};
+  for (int j = 0; j < n; ++j) {
+    if (!src_ptrs[j]) return MOE_EINVAL;
+    p.src[j] = static_cast<const uint8_t*>(src_ptrs[j]);
+  }
+  return status_of(launch_gather_group(p, n, expert_bytes, static_cast<uint8_t*>(group_buf),
+                                       first_pos, pos_stride, as_stream(stream)));
+}
+
+int moe_mmq_grouped(int wtype, const void* group_buf, size_t pos_stride, size_t mat_offset,
+                    int n_out, int k_in, const int32_t* group_experts, int n_group,
+                    const int32_t* offsets, int E, const void* act_q8, int epilogue, void* out,
+                    float* debug_h, void* stream) {
+  if (!group_buf || !group_experts || !offsets || !act_q8 || !out) return MOE_EINVAL;
+  if (n_group < 1 || n_group > MOE_MAX_GROUP || E < 1) return MOE_EINVAL;
+  if (epilogue < MOE_EPI_F32 || epilogue > MOE_EPI_I32_BLOCKDOTS) return MOE_EINVAL;
+  if (!valid_wtype(wtype)) return MOE_EUNSUPPORTED;
+  if (n_out < 128 || n_out % 128 != 0 || k_in < 128 || k_in % 128 != 0) return MOE_EUNSUPPORTED;
+  if (!aligned(group_buf, 4) || pos_stride % 4 != 0 || mat_offset % 4 != 0 ||
+      !aligned(act_q8, 16) || !aligned(out, 4) || !aligned(debug_h, 4))
+    return MOE_EINVAL;
+  MmqProblem p{};
+  p.wtype = wtype;
+  p.epilogue = epilogue;
+  p.wbase = static_cast<const uint8_t*>(group_buf);
+  p.pos_stride = pos_stride;
+  p.mat_offset = mat_offset;
+  p.n_out = n_out;
+  p.k_in = k_in;
+  p.act = static_cast<const uint8_t*>(act_q8);
+  p.out = out;
+  p.debug_h = debug_h;
+  p.offsets = offsets;
+  p.n_group = n_group;
+  for (int j = 0; j < n_group; ++j) {
+    if (group_experts[j] < 0 || group_experts[j] >= E) return MOE_EINVAL;
+    p.experts[j] = group_experts[j];
+  }
+  return status_of(launch_mmq(p, as_stream(stream)));
+}
+
+int moe_combine(const float* Dm, const int32_t* slot, const float* topk_w, int T, int K, int H,
+                float* out, void* stream) {
+  if (!Dm || !slot || !topk_w || !out || T < 1 || K < 1 || H < 4) return MOE_EINVAL;
+  if (!aligned(Dm, 16) || !aligned(out, 16)) return MOE_EINVAL;
+  if (H % 4 != 0 || K > MOE_MAX_K) return MOE_EUNSUPPORTED;
+  return status_of(launch_combine(Dm, slot, topk_w, T, K, H, out, as_stream(stream)));
+}
+
+int moe_prefill_layer(const float* x, int T, int H, int F, int E, int K, const int32_t* topk_idx,
+                      const float* topk_w, int wtype, const void* pool, const int64_t* expert_off,
+                      size_t expert_bytes, int group_size, int ring_start, void* ws,
+                      size_t ws_bytes, float* out, void* stream) {
+  if (!x || !topk_idx || !topk_w || !pool || !expert_off || !ws || !out) return MOE_EINVAL;
+  if (T < 1 || K < 1 || E < 1 || K > E || group_size < 1 || group_size > MOE_MAX_GROUP ||
+      ring_start < 0 || ring_start >= E)
+    return MOE_EINVAL;
+  if (!valid_wtype(wtype)) return MOE_EUNSUPPORTED;
+  if (H < 128 || H % 128 != 0 || F < 128 || F % 128 != 0 || E > MOE_MAX_E || K > MOE_MAX_K)
+    return MOE_EUNSUPPORTED;
+  if ((long long)T * K > (1LL << 30)) return MOE_EUNSUPPORTED;
+  if (expert_bytes != moe_expert_bytes(H, F, wtype)) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256)) return MOE_EINVAL;
+  Layout L;
+  if (!make_layout(T, H, F, E, K, wtype, &L)) return MOE_EINVAL;
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+
+  hipStream_t s = as_stream(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  MapsOut mo{I32(L.counts), I32(L.offsets), I32(L.src), I32(L.slot), I32(L.order),
+             I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
+             I32(L.ntiles), kMmqRows};
+
+  hipEvent_t* ev = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_done < g_prof_calls) ev = &g_prof_ev[(size_t)(g_prof_done++) * kEvPerCall];
+  }
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+  };
+
+  hipError_t e;
+  mark(0);
+  if ((e = launch_build_maps(topk_idx, T, K, E, ring_start, mo, s)) != hipSuccess) return MOE_EHIP;
+  mark(1);
+  if ((e = launch_quantize(x, T, H, K, mo.slot, mo.src, 0, base + L.q8x, s)) != hipSuccess)
+    return MOE_EHIP;
+  mark(2);
+  if ((e = launch_gather_all(static_cast<const uint8_t*>(pool), expert_off, mo.order, mo.n_active,
+                             E, group_size, expert_bytes, base + L.groups, L.group_stride, s)) !=
+      hipSuccess)
+    return MOE_EHIP;
+  mark(3);
+  MmqProblem gu{};
+  gu.wtype = wtype;
+  gu.epilogue = MOE_EPI_SWIGLU_Q8_1;
+  gu.wbase = base + L.groups;
+  gu.pos_stride = L.group_stride;
+  gu.mat_offset = 0;
+  gu.n_out = F;
+  gu.k_in = H;
+  gu.act = base + L.q8x;
+  gu.out = base + L.hq8;
+  gu.tiles = mo.tiles;
+  gu.n_tiles = mo.n_tiles;
+  gu.max_tiles = L.max_tiles;
+  if ((e = launch_mmq(gu, s)) != hipSuccess) return MOE_EHIP;
+  mark(4);
+  MmqProblem dn = gu;
+  dn.epilogue = MOE_EPI_F32;
+  dn.mat_offset = (size_t)2 * F * (H / 32) * moe_block_bytes(wtype);
+  dn.n_out = H;
+  dn.k_in = F;
+  dn.act = base + L.hq8;
+  dn.out = base + L.dm;
+  if ((e = launch_mmq(dn, s)) != hipSuccess) return MOE_EHIP;
+  mark(5);
+  if ((e = launch_combine(reinterpret_cast<const float*>(base + L.dm), mo.slot, topk_w, T, K, H,
+                          out, s)) != hipSuccess)
+    return MOE_EHIP;
+  mark(6);
+  return MOE_OK;
+}
+
+int moe_profile_begin(int n_calls) {
+  if (n_calls < 1 || n_calls > 100000) return MOE_EINVAL;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  destroy_events();
+  g_prof_ev.resize((size_t)n_calls * kEvPerCall);
+  for (hipEvent_t& e : g_prof_ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      destroy_events();
+      return MOE_EHIP;
+    }
+  }
+  g_prof_calls = n_calls;
+  g_prof_done = 0;
+  return MOE_OK;
+}
+
+int moe_profile_end(float* ms, int max_calls) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int n = g_prof_done;
+  int rc = n;
+  if (n > 0) {
+    if (hipEventSynchronize(g_prof_ev[(size_t)n * kEvPerCall - 1]) != hipSuccess) rc = MOE_EHIP;
+    for (int c = 0; c < n && c < max_calls && rc >= 0 && ms; ++c)
+      for (int st = 0; st < MOE_N_STAGES; ++st) {
+        float v = 0.0f;
+        if (hipEventElapsedTime(&v, g_prof_ev[(size_t)c * kEvPerCall + st],
+                                g_prof_ev[(size_t)c * kEvPerCall + st + 1]) != hipSuccess)
+          rc = MOE_EHIP;
+        ms[(size_t)c * MOE_N_STAGES + st] = v;
+      }
+  }
+  destroy_events();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Host-side launchers of the gfx950 kernels.  Each returns hipSuccess or the launch error; the
+// C ABI in api.cpp validates arguments before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- a0 routing ----------------------------------------------------------------------------
+hipError_t launch_route_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w,
+                             hipStream_t s);
+
+// ---- a1 maps (counting sort in chunks of kMapChunk entries, one wavefront per chunk) --------
+constexpr int kMapChunk = 1024;
+inline int map_chunks(int R) { return (R + kMapChunk - 1) / kMapChunk; }
+
+// Tile list entry of the layer's MMQ: rows row0 .. row0+nrows-1 of active expert `ordinal`.
+struct MTile {
+  int32_t ordinal;
+  int32_t expert;
+  int32_t row0;
+  int32_t nrows;
+};
+
+struct MapsOut {
+  int32_t* counts;    // [E]
+  int32_t* offsets;   // [E+1]
+  int32_t* src;       // [R]
+  int32_t* slot;      // [R]
+  int32_t* order;     // [E]
+  int32_t* n_active;  // [1]
+  int32_t* hist;      // [chunks x E] scratch
+  MTile* tiles;       // [max tiles] or nullptr
+  int32_t* n_tiles;   // [1] or nullptr
+  int tile_rows;      // rows per m-tile
+};
+hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_start,
+                             const MapsOut& o, hipStream_t s);
+inline int max_mtiles(int R, int E, int tile_rows) { return R / tile_rows + (E < R ? E : R); }
+
+// ---- a2 quantise ----------------------------------------------------------------------------
+hipError_t launch_quantize(const float* x, int T, int H, int K, const int32_t* slot,
+                           const int32_t* src, int mode, uint8_t* q8, hipStream_t s);
+
+// ---- a3 gather ------------------------------------------------------------------------------
+struct GatherPtrs {
+  const uint8_t* src[16];
+};
+hipError_t launch_gather_group(const GatherPtrs& p, int n, size_t bytes, uint8_t* dst,
+                               int first_pos, size_t pos_stride, hipStream_t s);
+// Every group of the layer in one launch: active expert i (ring order) -> dst + i*stride.
+hipError_t launch_gather_all(const uint8_t* pool, const int64_t* expert_off,
+                             const int32_t* order, const int32_t* n_active, int max_slots,
+                             int group_size, size_t bytes, uint8_t* dst, size_t stride,
+                             hipStream_t s);
+
+// ---- a4..a6 MMQ -----------------------------------------------------------------------------
+constexpr int kMmqRows = 64;  // rows per m-tile
+
+struct MmqProblem {
+  int wtype;
+  int epilogue;           // 0 f32, 1 swiglu->q8_1, 2 int32 block dots
+  const uint8_t* wbase;   // group buffer(s)
+  size_t pos_stride;      // bytes between expert positions
+  size_t mat_offset;      // bytes from an expert's start to the matrix
+  int n_out;
+  int k_in;
+  const uint8_t* act;     // q8_1 rows of k_in values
+  void* out;
+  float* debug_h;
+  // layer form: device tile list
+  const MTile* tiles;
+  const int32_t* n_tiles;
+  int max_tiles;
+  // group form: positions j < n_group hold experts[j], rows from offsets
+  const int32_t* offsets;
+  int experts[16];
+  int n_group;
+};
+hipError_t launch_mmq(const MmqProblem& p, hipStream_t s);
+
+// ---- a7 combine -----------------------------------------------------------------------------
+hipError_t launch_combine(const float* Dm, const int32_t* slot, const float* w, int T, int K,
+                          int H, float* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,205 @@
+// a1  Token -> row maps.  "#1368 prefill: quantize each token's MoE input once and scatter it to
+// its k rows", opening section: src_dev names each of the T*K rows' source, and token t's k-th row
+// is slot[t*K+k], the inverse of src_dev.  Rows are grouped by expert id and keep ascending t*K+k
+// inside an expert, so the result is unique: a stable counting sort.
+//
+// Three launches, no host synchronisation:
+//   hist     one wavefront per chunk of kMapChunk entries: a per-chunk histogram in LDS.
+//   scan     one workgroup: per-expert exclusive prefix over chunks, counts, offsets, the ring
+//            order of the experts with rows and the m-tile list of the MMQ.
+//   scatter  one wavefront per chunk, 64 entries at a time in index order: ballots over the bits
+//            of the expert id give each lane its equal-id peers, mbcnt its rank among them, so
+//            rows are placed in ascending t*K+k without atomics.
+// Entries with an id outside [0, E) are skipped (a caller error; nothing is accessed out of
+// bounds, the maps are then incomplete).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kMaxE = 2048;   // largest E the single-workgroup scan holds in LDS
+
+__global__ __launch_bounds__(256) void maps_hist_kernel(const int32_t* __restrict__ idx, int R,
+                                                         int E, int nchunks,
+                                                         int32_t* __restrict__ hist) {
+  extern __shared__ int32_t lds_hist[];  // [4][E]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunk = blockIdx.x * 4 + wave;
+  int32_t* h = lds_hist + wave * E;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __syncthreads();
+  if (chunk < nchunks) {
+    const int base = chunk * kMapChunk;
+    for (int it = 0; it < kMapChunk / 64; ++it) {
+      const int i = base + it * 64 + lane;
+      if (i < R) {
+        const int e = idx[i];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (chunk < nchunks)
+    for (int e = lane; e < E; e += 64) hist[(size_t)chunk * E + e] = h[e];
+}
+
+// Exclusive prefix of n ints (n <= 2 * kScanThreads) held as lds[0..n), in place; returns the
+// total to every thread.
+__device__ int block_exclusive_scan(int32_t* lds, int n, int32_t* wave_sums) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int a = i0 < n ? lds[i0] : 0;
+  const int b = i1 < n ? lds[i1] : 0;
+  int v = a + b;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int nw = kScanThreads / 64;
+    int s = lane < nw ? wave_sums[lane] : 0;
+    int si = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(si, off);
+      if (lane >= off) si += o;
+    }
+    if (lane < nw) wave_sums[lane] = si - s;  // exclusive wave offsets
+    if (lane == nw - 1) wave_sums[nw] = si;   // total
+  }
+  __syncthreads();
+  const int excl = wave_sums[wave] + incl - v;
+  const int total = wave_sums[kScanThreads / 64];
+  if (i0 < n) lds[i0] = excl;
+  if (i1 < n) lds[i1] = excl + a;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kScanThreads) void maps_scan_kernel(
+    int E, int nchunks, int ring_start, int32_t* __restrict__ hist, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ order, int32_t* __restrict__ n_active,
+    MTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int tile_rows) {
+  __shared__ int32_t s_cnt[kMaxE];   // rows of expert e
+  __shared__ int32_t s_off[kMaxE];   // first row of expert e
+  __shared__ int32_t s_act[kMaxE];   // ring position j -> ordinal among the experts with rows
+  __shared__ int32_t s_til[kMaxE];   // ring position j -> its first m-tile
+  __shared__ int32_t s_wsum[kScanThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  // per expert: exclusive prefix over chunks (in place), and the count
+  for (int e = tid; e < E; e += kScanThreads) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = hist[(size_t)c * E + e];
+      hist[(size_t)c * E + e] = run;
+      run += v;
+    }
+    s_cnt[e] = run;
+    s_off[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  const int R = block_exclusive_scan(s_off, E, s_wsum);
+  for (int e = tid; e < E; e += kScanThreads) offsets[e] = s_off[e];
+  if (tid == 0) offsets[E] = R;
+  // ring order of the experts with rows, and their m-tiles
+  for (int j = tid; j < E; j += kScanThreads) {
+    const int c = s_cnt[(ring_start + j) % E];
+    s_act[j] = c > 0 ? 1 : 0;
+    s_til[j] = (c + tile_rows - 1) / tile_rows;
+  }
+  __syncthreads();
+  const int nact = block_exclusive_scan(s_act, E, s_wsum);
+  const int nt = block_exclusive_scan(s_til, E, s_wsum);
+  for (int j = tid; j < E; j += kScanThreads) {
+    const int e = (ring_start + j) % E;
+    const int c = s_cnt[e];
+    if (c == 0) continue;
+    order[s_act[j]] = e;
+    if (tiles == nullptr) continue;
+    for (int m = 0; m * tile_rows < c; ++m) {
+      MTile tl;
+      tl.ordinal = s_act[j];
+      tl.expert = e;
+      tl.row0 = s_off[e] + m * tile_rows;
+      tl.nrows = min(tile_rows, c - m * tile_rows);
+      tiles[s_til[j] + m] = tl;
+    }
+  }
+  if (tid == 0) {
+    *n_active = nact;
+    if (n_tiles != nullptr) *n_tiles = nt;
+  }
+}
+
+__global__ __launch_bounds__(256) void maps_scatter_kernel(const int32_t* __restrict__ idx, int R,
+                                                            int E, int nbits, int nchunks,
+                                                            const int32_t* __restrict__ hist,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ src,
+                                                            int32_t* __restrict__ slot) {
+  extern __shared__ int32_t lds_ctr[];  // [4][E]: each wavefront's next free row per expert
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunk = blockIdx.x * 4 + wave;
+  const bool live = chunk < nchunks;
+  int32_t* ctr = lds_ctr + wave * E;
+  if (live)
+    for (int e = lane; e < E; e += 64) ctr[e] = offsets[e] + hist[(size_t)chunk * E + e];
+  __syncthreads();
+  if (!live) return;
+  // From here each wavefront touches only its own counters; LDS operations of one wavefront
+  // complete in issue order, so no further barrier is needed.
+  const int base = chunk * kMapChunk;
+  for (int it = 0; it < kMapChunk / 64; ++it) {
+    const int i = base + it * 64 + lane;
+    const int e = i < R ? idx[i] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    uint64_t peers = ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = ballot(bit);
+      peers &= bit ? ones : ~ones;
+    }
+    const int rank = mbcnt(peers);   // equal-id lanes below this one
+    const int cnt = __popcll(peers);
+    if (valid) {
+      const int r = ctr[e] + rank;
+      src[r] = i;
+      slot[i] = r;
+      if (rank == 0) ctr[e] = r + cnt;   // after every lane's read above (one instruction stream)
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_start,
+                             const MapsOut& o, hipStream_t s) {
+  const int R = T * K;
+  const int nchunks = map_chunks(R);
+  const int blocks = (nchunks + 3) / 4;
+  const size_t lds = (size_t)4 * E * sizeof(int32_t);
+  maps_hist_kernel<<<blocks, 256, lds, s>>>(idx, R, E, nchunks, o.hist);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  maps_scan_kernel<<<1, kScanThreads, 0, s>>>(E, nchunks, ring_start, o.hist, o.counts, o.offsets,
+                                              o.order, o.n_active, o.tiles, o.n_tiles,
+                                              o.tile_rows);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  maps_scatter_kernel<<<blocks, 256, lds, s>>>(idx, R, E, nbits, nchunks, o.hist, o.offsets,
+                                               o.src, o.slot);
+  return hipGetLastError();
+}
+
+}  // namespace moe

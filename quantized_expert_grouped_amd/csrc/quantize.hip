@@ -1,0 +1,111 @@
+// a2  q8_1 quantisation of the layer input.  "#1368 prefill: quantize each token's MoE input once
+// and scatter it to its k rows (the same bytes)", opening section: the per-row form quantises
+// the T*K rows in expert order and so reads each token's input K times; the scatter form
+// quantises each token once and writes the same block to every row slot[t*K+k].
+//
+// Block arithmetic (identical in both forms): amax = max|v|; d = amax/127 (IEEE division);
+// q = roundf(v/d) (IEEE division, ties away from zero); S = sum q; stored d16 = fp16(d),
+// s16 = fp16(d * S); an all-zero block stores zeros.  Row layout (DS4): 144 B per 128 values =
+// 4 x (d16, s16) then 4 x 32 q.
+//
+// One wavefront per token (scatter) or per row (per-row form).  A lane owns 16 consecutive
+// values (four coalesced float4 loads), so a block of 32 is a lane pair: one xor-shuffle for
+// amax and one for S.  Each lane then stores its 16 q bytes with one 16-byte store per
+// destination row, and the first lane of each 8-lane group the group's 16-byte (d, s) header.
+#include <math.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+namespace {
+
+template <int MODE>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ x, int T, int H,
+                                                       int K, const int32_t* __restrict__ slot,
+                                                       const int32_t* __restrict__ src,
+                                                       uint8_t* __restrict__ q8) {
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nunits = MODE == 0 ? T : T * K;
+  if (unit >= nunits) return;  // uniform per wavefront
+  const int t = MODE == 0 ? unit : src[unit] / K;
+  const float* xr = x + (size_t)t * H;
+  const size_t rb = (size_t)(H / kDs4Vals) * kDs4Bytes;
+  int my_row = unit;
+  if (MODE == 0) my_row = lane < K ? slot[(size_t)t * K + lane] : 0;
+  const int nrows = MODE == 0 ? K : 1;
+
+  for (int c0 = 0; c0 < H; c0 += 64 * 16) {
+    const int v0 = c0 + lane * 16;
+    const bool act = v0 < H;  // H is a multiple of 128: whole 8-lane groups
+    float v[16];
+    if (act) {
+      const float4* p = reinterpret_cast<const float4*>(xr + v0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = p[i];
+        v[4 * i + 0] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    const bool nz = am > 0.0f;
+    const float d = am / 127.0f;
+    int S = 0;
+    uint32_t qw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int q = nz ? (int)roundf(v[4 * i + b] / d) : 0;
+        S += q;
+        packed |= (uint32_t)(q & 0xff) << (8 * b);
+      }
+      qw[i] = packed;
+    }
+    S += __shfl_xor(S, 1);
+    const uint32_t hdr = nz ? (f2h(d) | (q8_1_scale_bits(d, S) << 16)) : 0u;
+    const uint32_t h1 = __shfl_down(hdr, 2);
+    const uint32_t h2 = __shfl_down(hdr, 4);
+    const uint32_t h3 = __shfl_down(hdr, 6);
+    const int g = v0 / kDs4Vals;
+    const size_t hoff = (size_t)g * kDs4Bytes;
+    const size_t qoff = hoff + 16 + ((lane & 7) >> 1) * 32 + (lane & 1) * 16;
+    const uint4 qv = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+    const uint4 hv = make_uint4(hdr, h1, h2, h3);
+    for (int k = 0; k < nrows; ++k) {
+      const int r = MODE == 0 ? __shfl(my_row, k) : my_row;
+      uint8_t* row = q8 + (size_t)r * rb;
+      if (act) {
+        *reinterpret_cast<uint4*>(row + qoff) = qv;
+        if ((lane & 7) == 0) *reinterpret_cast<uint4*>(row + hoff) = hv;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float* x, int T, int H, int K, const int32_t* slot,
+                           const int32_t* src, int mode, uint8_t* q8, hipStream_t s) {
+  const int nunits = mode == 0 ? T : T * K;
+  const dim3 grid((nunits + 3) / 4), block(256);
+  if (mode == 0)
+    quantize_kernel<0><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
+  else
+    quantize_kernel<1><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,143 @@
+"""GPU parity: the whole layer (moe_prefill_layer) against the oracle, with its intermediate
+buffers, the invariances the pages state, and edge cases."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, host, note, rel_err
+from quantized_expert_grouped_amd import abi, synth
+from quantized_expert_grouped_amd.layer import MoePrefillLayer
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3   # max |gpu - oracle| <= 1e-3 * max |oracle|
+
+
+def _layer(c, **kw):
+    return MoePrefillLayer(c.pool, c.expert_off, c.H, c.F, c.E, c.wtype, c.T, c.K,
+                           group_size=kw.get("group_size", 16),
+                           ring_start=kw.get("ring_start", c.ring_start))
+
+
+def _run(layer, c, idx, w, **kw):
+    note(f"layer {c.name} T={c.T} H={c.H} F={c.F} E={c.E} K={c.K} wtype={c.wtype} {kw}")
+    out = layer.forward(dev(c.x), dev(idx), dev(w), **kw)
+    return host(out)
+
+
+CASES = [
+    # name, T, H, F, E, K, wtype, zipf
+    ("tiny", 7, 256, 128, 16, 2, synth.Q8_0, None),
+    ("tiny_q4_1", 7, 256, 128, 16, 2, synth.Q4_1, None),
+    ("ragged", 301, 512, 256, 24, 4, synth.Q8_0, None),
+    ("ragged_q4_1", 301, 512, 256, 24, 4, synth.Q4_1, None),
+    ("skew", 403, 256, 384, 32, 3, synth.Q4_1, 1.2),
+    ("wide", 64, 1024, 128, 8, 8, synth.Q8_0, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_layer_against_oracle(orc, case):
+    name, T, H, F, E, K, wtype, zipf = case
+    c = synth.make_case(name, T=T, H=H, F=F, E=E, K=K, wtype=wtype, seed=zlib.crc32(name.encode()) % 10000,
+                        zero_tokens=(T // 3,), zipf=zipf)
+    idx, w = orc.route_topk(c.logits, K)
+    want, dbg = orc.prefill_layer(c.x, idx, w, wtype, c.pool, c.expert_off, F, E, debug=True)
+    layer = _layer(c)
+    got = _run(layer, c, idx, w)
+    assert rel_err(got, want) <= TOL
+    assert not got[T // 3].any()                      # an all-zero token: an exact zero row
+    # intermediate results in the workspace
+    R = T * K
+    m = orc.build_maps(idx, E, c.ring_start)
+    ws = host(layer.ws)
+
+    def region(which, nbytes):
+        o = abi.workspace_offset(which, T, H, F, E, K, wtype, 16)
+        return ws[o:o + nbytes]
+
+    assert np.array_equal(region(abi.WS_COUNTS, 4 * E).view(np.int32), m["counts"])
+    assert np.array_equal(region(abi.WS_OFFSETS, 4 * (E + 1)).view(np.int32), m["offsets"])
+    assert np.array_equal(region(abi.WS_SRC, 4 * R).view(np.int32), m["src"])
+    assert np.array_equal(region(abi.WS_SLOT, 4 * R).view(np.int32), m["slot"])
+    n = int(region(abi.WS_NACTIVE, 4).view(np.int32)[0])
+    assert n == m["n_active"]
+    assert np.array_equal(region(abi.WS_ORDER, 4 * E).view(np.int32)[:n], m["order"])
+    xrb = abi.q8_1_row_bytes(H)
+    assert np.array_equal(region(abi.WS_Q8X, R * xrb).reshape(R, xrb), dbg["q8x"])
+    stride = abi.workspace_offset(abi.WS_GROUP_STRIDE, T, H, F, E, K, wtype, 16)
+    groups = region(abi.WS_GROUPS, n * stride).reshape(n, stride)
+    for i, e in enumerate(m["order"]):
+        assert np.array_equal(groups[i, :c.expert_bytes], c.expert(e)), (i, e)
+    Dm = region(abi.WS_DM, R * H * 4).view(np.float32).reshape(R, H)
+    assert rel_err(Dm, dbg["Dm"]) <= TOL
+
+
+def test_layer_bit_identical_over_group_size_and_ring_start(orc):
+    """The same bytes land in the same places whatever the grouping and where the ring walk
+    starts: the output is bitwise identical."""
+    c = synth.make_case("inv", T=257, H=256, F=256, E=40, K=5, wtype=synth.Q4_1, seed=5,
+                        zipf=0.9)
+    idx, w = orc.route_topk(c.logits, c.K)
+    layer = _layer(c, group_size=16, ring_start=0)
+    ref = _run(layer, c, idx, w, group_size=16, ring_start=0)
+    for gs, rs in [(1, 0), (5, 7), (16, 39), (3, 20), (16, 1)]:
+        got = _run(layer, c, idx, w, group_size=gs, ring_start=rs)
+        assert np.array_equal(got, ref), (gs, rs)
+
+
+def test_layer_token_permutation_equivariance(orc):
+    c = synth.make_case("perm", T=200, H=256, F=128, E=16, K=3, wtype=synth.Q8_0, seed=6)
+    idx, w = orc.route_topk(c.logits, c.K)
+    layer = _layer(c)
+    ref = _run(layer, c, idx, w)
+    p = np.random.default_rng(1).permutation(c.T)
+    c2 = synth.make_case("perm", T=200, H=256, F=128, E=16, K=3, wtype=synth.Q8_0, seed=6)
+    c2.x = c.x[p].copy()
+    got = _run(layer, c2, idx[p].copy(), w[p].copy())
+    assert np.array_equal(got, ref[p])
+
+
+@pytest.mark.parametrize("edge", ["T1", "K_eq_E", "E1", "one_expert_takes_all", "half_empty"])
+def test_layer_edge_cases(orc, edge):
+    T, H, F, E, K, wtype = 50, 256, 128, 8, 2, synth.Q8_0
+    if edge == "T1":
+        T = 1
+    if edge == "K_eq_E":
+        E, K = 6, 6
+    if edge == "E1":
+        E, K = 1, 1
+    c = synth.make_case(edge, T=T, H=H, F=F, E=E, K=K, wtype=wtype, seed=len(edge))
+    if edge == "one_expert_takes_all":
+        c.logits[:, 5] += 100.0
+        K = 1
+        c.K = 1
+    if edge == "half_empty":
+        c.logits[:, :4] -= 100.0
+    idx, w = orc.route_topk(c.logits, c.K)
+    want = orc.prefill_layer(c.x, idx, w, wtype, c.pool, c.expert_off, F, E)
+    layer = _layer(c, ring_start=0)
+    got = _run(layer, c, idx, w, ring_start=0)
+    assert rel_err(got, want) <= TOL
+
+
+def test_layer_step_with_gpu_routing(orc):
+    """Routing and the layer in one pass on the GPU (the benchmark's step)."""
+    c = synth.make_case("step", T=300, H=512, F=256, E=32, K=4, wtype=synth.Q4_1, seed=8)
+    layer = _layer(c)
+    note("layer step with routing")
+    out = host(layer.step(dev(c.x), dev(c.logits)))
+    idx, w = orc.route_topk(c.logits, c.K)
+    want = orc.prefill_layer(c.x, idx, w, c.wtype, c.pool, c.expert_off, c.F, c.E)
+    assert rel_err(out, want) <= TOL
+
+
+def test_layer_repeat_is_deterministic(orc):
+    c = synth.make_case("rep", T=128, H=256, F=128, E=16, K=4, wtype=synth.Q4_1, seed=9)
+    idx, w = orc.route_topk(c.logits, c.K)
+    layer = _layer(c)
+    a = _run(layer, c, idx, w)
+    b = _run(layer, c, idx, w)
+    assert np.array_equal(a, b)

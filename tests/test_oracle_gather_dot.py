@@ -87,3 +87,17 @@ def test_block_dots_matrix(orc, wtype):
     qx, _, _ = npref.q8_1_decode(act, k_in)
     want = np.einsum("nbj,rbj->rnb", q.reshape(n_out, -1, 32), qx.reshape(rows, -1, 32))
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+def test_mmq_rows_matrix_form(orc, wtype):
+    """The products of many rows against numpy's matrix form (d*q dequantised, plus m @ s)."""
+    rng = np.random.default_rng(18 + wtype)
+    n_out, k_in = 9, 384
+    wmat = _block(wtype, rng, n_out * k_in // 32).reshape(-1)
+    act = orc.q8_1_rows(rng.standard_normal((5, k_in)).astype(np.float32))
+    got = orc.mmq_rows(wtype, wmat, n_out, k_in, act)
+    parts = npref.matrix_parts(wmat, n_out, k_in, wtype)
+    for r in range(5):
+        want = npref.qproduct(parts, act[r], k_in)
+        assert np.allclose(got[r], want, rtol=1e-12, atol=1e-12)
