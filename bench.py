@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the prefill MoE expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t8k]
+
+A step is one pass of the whole hot path over one chunk of synthetic input already resident in
+HBM: top-K routing from the router logits, then the layer (maps, q8_1 quantise-scatter, every
+group's gather, MMQ gate/up with SwiGLU and requantisation, MMQ down, combine).  The metric is
+routed rows per second (T*K rows per step).  Prints one JSON line.
+
+Per-stage HIP events recorded on the layer's own stream give each kernel's duration; the
+dominant kernel's roofline fraction uses its algorithmic work (ops or bytes) per launch.  The
+CPU baseline times the plain C oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from quantized_expert_grouped_amd import abi, synth  # noqa: E402
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0          # HBM3E, GB/s
+PEAK_I8_TOPS = 5000.0          # dense int8 MFMA, TOP/s (counted as 2 ops per multiply-add)
+
+WORKLOAD_DOC = {
+    "tiny": "T=7 H=256 F=128 E=16 K=2 Q8_0",
+    "t2k": "T=2048 H=2048 F=512 E=512 K=10 Q8_0, uniform routing",
+    "t8k": "T=8192 H=2048 F=512 E=512 K=10 Q4_1, uniform routing",
+    "t32k": "T=32768 H=2048 F=512 E=512 K=10 Q8_0, uniform routing",
+    "t30k_zipf": "T=30118 H=2048 F=512 E=512 K=10 Q4_1, Zipf-skewed routing",
+}
+
+
+def algorithmic_work(c, n_active: int):
+    """Per-launch algorithmic work of each stage: (kind, amount) with kind 'ops' or 'bytes'.
+
+    Bytes count each operand read once and each result written once; ops count two per
+    multiply-add of the integer block dots."""
+    T, H, F, E, K = c.T, c.H, c.F, c.E, c.K
+    R = T * K
+    xrb = abi.q8_1_row_bytes(H)
+    hrb = abi.q8_1_row_bytes(F)
+    eb = c.expert_bytes
+    gu_bytes = 2 * F * (H // 32) * synth.BLOCK_BYTES[c.wtype]
+    dn_bytes = eb - gu_bytes
+    return {
+        "route": ("bytes", 4 * T * E + 8 * R),
+        "maps": ("bytes", 4 * R + 3 * 4 * R + 8 * E),
+        "quantize": ("bytes", 4 * T * H + 4 * R + R * xrb),
+        "gather": ("bytes", 2 * n_active * eb),
+        "gate_up": ("ops", 4 * R * F * H),
+        "down": ("ops", 2 * R * H * F),
+        "combine": ("bytes", 4 * R * H + 8 * R + 4 * T * H),
+        # memory side of the MMQ launches, for reference
+        "gate_up_bytes": ("bytes", n_active * gu_bytes + R * xrb + R * hrb),
+        "down_bytes": ("bytes", n_active * dn_bytes + R * hrb + 4 * R * H),
+    }
+
+
+def cpu_baseline(c, idx, w, target_s: float = 12.0):
+    """Time the oracle (as it stands) on the first tokens of the same workload."""
+    import oracle
+    oracle.lib()
+    threads = oracle.get_threads()
+    # size the sample from a short probe so that the measured run takes ~target_s
+    probe_t = 16
+    t0 = time.perf_counter()
+    oracle.prefill_layer(c.x[:probe_t], idx[:probe_t], w[:probe_t], c.wtype, c.pool,
+                         c.expert_off, c.F, c.E)
+    dt = time.perf_counter() - t0
+    n_tok = int(min(c.T, max(probe_t, probe_t * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.prefill_layer(c.x[:n_tok], idx[:n_tok], w[:n_tok], c.wtype, c.pool, c.expert_off, c.F,
+                         c.E)
+    dt = time.perf_counter() - t0
+    rows = n_tok * c.K
+    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tok} tokens of {c.name} ({rows} routed rows): the whole oracle "
+                      f"layer (maps, q8_1 scatter, every routed row through its expert, combine) "
+                      f"in {dt:.2f} s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t8k", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--no-stage-events", action="store_true",
+                    help="time the steps without the per-stage events")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by token chunks with no exchange: each GPU would run its own "
+              "chunk, so the one-GPU figure is the per-GPU rate)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_expert_grouped_amd.layer import MoePrefillLayer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = synth.config_case(args.workload)
+    layer = MoePrefillLayer(c.pool, c.expert_off, c.H, c.F, c.E, c.wtype, c.T, c.K,
+                            group_size=16, ring_start=c.ring_start, device=dev)
+    x = torch.from_numpy(c.x).to(dev)
+    logits = torch.from_numpy(c.logits).to(dev)
+    out = torch.empty((c.T, c.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.step(x, logits, out)
+    torch.cuda.synchronize()
+
+    use_events = not args.no_stage_events
+    if use_events:
+        abi.profile_begin(args.steps)
+        ev_route = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if use_events:
+            ev_route[i][0].record(stream)
+            idx, w = layer.route(logits)
+            ev_route[i][1].record(stream)
+            layer.forward(x, idx, w, out)
+        else:
+            layer.step(x, logits, out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    rows = c.T * c.K
+    value = rows * args.steps / elapsed
+
+    n_active = int(layer.ws_view(abi.WS_NACTIVE, c.T, 4).view(torch.int32).item())
+    work = algorithmic_work(c, n_active)
+    stages = {}
+    roofline = None
+    if use_events:
+        ms = abi.profile_end(args.steps)               # [steps, 6]
+        route_ms = np.array([a.elapsed_time(b) for a, b in ev_route])
+        avg = dict(zip(abi.STAGES, ms.mean(axis=0).tolist()))
+        avg = {"route": float(route_ms.mean()), **avg}
+        for name, t_ms in avg.items():
+            entry = {"ms": round(t_ms, 4)}
+            if name in work:
+                kind, amt = work[name]
+                if kind == "ops":
+                    entry["tops"] = round(amt / (t_ms * 1e-3) / 1e12, 2)
+                    entry["frac_i8_peak"] = round(entry["tops"] / PEAK_I8_TOPS, 4)
+                    kb, bb = work[name + "_bytes"]
+                    entry["gbs"] = round(bb / (t_ms * 1e-3) / 1e9, 1)
+                else:
+                    entry["gbs"] = round(amt / (t_ms * 1e-3) / 1e9, 1)
+                    entry["frac_hbm_peak"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
+            stages[name] = entry
+        dom = max(avg, key=avg.get)
+        kind, amt = work.get(dom, ("bytes", 4 * c.R))
+        t_s = avg[dom] * 1e-3
+        if kind == "ops":
+            achieved = amt / t_s / 1e12
+            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                        "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": None}
+        else:
+            achieved = amt / t_s / 1e9
+            roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        idx_d, w_d = layer.route(logits)
+        cpu = cpu_baseline(c, idx_d.cpu().numpy(), w_d.cpu().numpy())
+
+    line = {
+        "metric": "routed rows/sec (TxK) for the MoE prefill layer",
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}", "T": c.T, "H": c.H,
+                   "F": c.F, "E": c.E, "K": c.K, "wtype": synth.WTYPE_NAME[c.wtype],
+                   "group_size": 16, "active_experts": n_active, "stage_events": use_events},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
