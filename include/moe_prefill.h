@@ -122,7 +122,7 @@ int moe_gather_group(const void *const *src_ptrs, int n, size_t expert_bytes, vo
  *   MOE_EPI_SWIGLU_Q8_1:   q8_1 rows of h = silu(g)*u (n_out values); debug_h, if not NULL, gets the
  *                          fp32 h [* x n_out] that was quantised
  *   MOE_EPI_I32_BLOCKDOTS: int32 [* x n_out x k_in/32], the raw I_b
- * n_out and k_in: multiples of 128.  group_buf, pos_stride and mat_offset: multiples of 4 bytes;
+ * n_out and k_in: multiples of 128.  group_buf, pos_stride and mat_offset: multiples of 16 bytes;
  * act_q8: 16-byte aligned.  The matrix must lie inside each position's bytes (caller's duty). */
 int moe_mmq_grouped(int wtype, const void *group_buf, size_t pos_stride, size_t mat_offset,
                     int n_out, int k_in, const int32_t *group_experts, int n_group,

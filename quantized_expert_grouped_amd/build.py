@@ -32,6 +32,9 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed fp32 instructions on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the scale epilogue reads them with plain VALU operands instead of
+    # a v_accvgpr_read per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
     "-I", INCLUDE, "-I", CSRC,
 ]

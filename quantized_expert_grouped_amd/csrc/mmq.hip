@@ -5,22 +5,30 @@
 // section: the down projection's input is quantised to q8_1 again.
 //
 // For weight row n and activation row r, block b (32 values):
-//   I_b = sum_j qw_j * qx_j                      (exact int32, v_mfma_i32_32x32x32_i8: K = 32
-//                                                 is exactly one block)
-//   y_b = dw * dx * I_b   (+ mw * sx for Q4_1)   (fp32, fused multiply-adds, b ascending)
-// Each output element is accumulated by one lane in one fixed order whatever the tiling, so
-// results do not depend on group size, ring start or the row's place in its tile.
+//   I_b = sum_j qw_j * qx_j                 exact int32: one v_mfma_i32_32x32x32_i8 per block
+//                                           (K = 32 is exactly one block)
+//   S_b = dx_b * dw_b                       exact in fp32 (two fp16 significands): for a whole
+//                                           32x32 tile this is an outer product, one
+//                                           v_mfma_f32_32x32x16_f16 with a single nonzero k
+//   acc = fma(float(I_b), S_b, acc)         the only per-element VALU work (convert + fma)
+//   Q4_1 adds sum_b mw_b * sx_b             a true sum over blocks: an f16 MFMA whose C input
+//                                           is the accumulator itself
+// Blocks are taken in ascending order and every output element is accumulated by one lane in
+// one fixed instruction sequence, so results do not depend on the tiling, the group size, the
+// ring start or the row's place in its tile.
 //
-// Workgroup tile: 64 activation rows (one m-tile of one expert) x 128 weight rows, 4 wavefronts.
-// Wavefront (wr, wc) computes rows 32*wr.. with two 32x32 MFMA tiles:
-//   MOE_EPI_SWIGLU_Q8_1: gate rows f0+32wc.. and up rows F+f0+32wc.. (the same 32 features), so
+// Workgroup: 64 activation rows (one m-tile of one expert) x 128 weight rows, 4 wavefronts.
+// Wavefront (wr, wc) owns rows 32*wr.. and two 32-row column tiles of the weights:
+//   MOE_EPI_SWIGLU_Q8_1: gate features f0+32wc.. and the up rows of the same features, so
 //     h = silu(g) * u is formed in registers and requantised along F across the 32 lanes that
 //     hold one block of 32 features;
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
-// K loop: 4 blocks (128 values, one q8_1 group) per LDS stage.  Weights are unpacked while
-// staging: Q8_0's 34-byte blocks are realigned with v_alignbit, Q4_1's nibbles are split into
-// bytes (element j low nibble, j+16 high), so both types feed the same int8 MFMA; per-block
-// scales are converted to fp32 tables in LDS.
+// K loop: stages of 4 blocks (128 values, one q8_1 group).  The next stage's global loads are
+// issued before the current stage's MFMAs and land in the other half of a double-buffered LDS,
+// so each stage costs one barrier.  Weights are unpacked while staging: Q8_0's 34-byte blocks
+// are realigned with v_alignbit, Q4_1's nibbles split into bytes (element j low nibble, j+16
+// high), so both types feed the same int8 MFMA.  Scales stay fp16 bits, laid out in LDS as the
+// f16 MFMA operands (with the unused k slots zero).
 #include <math.h>
 
 #include "common.hpp"
@@ -32,94 +40,132 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-constexpr int kRowsM = kMmqRows;   // 64 activation rows per workgroup
-constexpr int kRowsN = 128;        // weight rows per workgroup
-constexpr int kKB = 4;             // blocks per stage
-constexpr int kAStride = 144;      // LDS bytes per activation row (the raw q8_1 group)
-constexpr int kBStride = 144;      // LDS bytes per weight row (4 x 32 unpacked int8 + pad)
+constexpr int kRowsM = kMmqRows;  // 64 activation rows per workgroup
+constexpr int kRowsN = 128;       // weight rows per workgroup
+constexpr int kKB = 4;            // blocks per stage
+constexpr int kStride = 144;      // LDS bytes per row of q: 4 x 32 + 16 of padding
 
-struct Lds {
-  uint8_t a[kRowsM * kAStride];
-  float dx[kKB][kRowsM];
-  float sx[kKB][kRowsM];
-  uint8_t b[kRowsN * kBStride];
-  float dw[kKB][kRowsN];
-  float mw[kKB][kRowsN];
+struct Buf {
+  uint8_t aq[kRowsM * kStride];   // activation q, [row][block][32]
+  uint8_t bq[kRowsN * kStride];   // weight q as int8, [row][block][32]
+  uint16_t dx[kKB][2][64];        // [block][row tile][lane]: d of row (lane < 32), else 0
+  uint16_t dw[kKB][4][64];        // [block][col tile][lane]: d of weight row, else 0
+  uint16_t sx[2][64][8];          // [row tile][lane][k]: s of the stage's 4 blocks, rest 0
+  uint16_t mw[4][64][8];          // [col tile][lane][k]: m of the stage's 4 blocks, rest 0
 };
 
+struct Stage {  // one thread's share of a stage's global loads, held in registers
+  uint4 a[3];
+  uint32_t w[17];
+};
+
+__device__ __forceinline__ int weight_row(int epi, int nb, int n0, int n_out) {
+  // SwiGLU tiles hold gate features n0.. in LDS rows 0..63 and the same up features in 64..127
+  return epi == 1 ? (nb < 64 ? n0 + nb : n_out + n0 + nb - 64) : n0 + nb;
+}
+
 template <int WT>
-__device__ __forceinline__ void stage_weights(Lds& L, const uint8_t* __restrict__ W,
-                                              size_t row_bytes, int stage, int epi, int n0,
-                                              int n_out) {
+__device__ __forceinline__ void load_stage(Stage& st, const uint8_t* __restrict__ act,
+                                           size_t act_row_bytes, int row0, int nrows,
+                                           const uint8_t* __restrict__ W, size_t row_bytes,
+                                           int s, int epi, int n0, int n_out) {
   const int tid = threadIdx.x;
-  if (WT == 0) {
-    // 128 rows x 2 pairs of 34-byte blocks = 256 items, 17 dwords each
-    const int nb = tid >> 1, pair = tid & 1;
-    const int wrow = epi == 1 ? (nb < 64 ? n0 + nb : n_out + n0 + nb - 64) : n0 + nb;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        W + (size_t)wrow * row_bytes + (size_t)stage * (kKB * 34) + pair * 68);
-    uint32_t w[17];
 #pragma unroll
-    for (int i = 0; i < 17; ++i) w[i] = src[i];
+  for (int j = 0; j < 3; ++j) {
+    const int c = tid + 256 * j;  // 64 rows x 9 chunks of 16 bytes
+    const int row = c / 9, part = c - row * 9;
+    st.a[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < kRowsM * 9 && row < nrows)
+      st.a[j] = *reinterpret_cast<const uint4*>(act + (size_t)(row0 + row) * act_row_bytes +
+                                                (size_t)s * kDs4Bytes + part * 16);
+  }
+  const int nb = tid >> 1, pair = tid & 1;  // 128 weight rows x 2 pairs of blocks
+  const uint8_t* src = W + (size_t)weight_row(epi, nb, n0, n_out) * row_bytes;
+  if (WT == 0) {
+    const uint32_t* p =
+        reinterpret_cast<const uint32_t*>(src + (size_t)s * (kKB * 34) + pair * 68);
+#pragma unroll
+    for (int i = 0; i < 17; ++i) st.w[i] = p[i];
+  } else {
+    const uint2* p =
+        reinterpret_cast<const uint2*>(src + (size_t)(s * kKB + 2 * pair) * 20);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint2 v = p[i];
+      st.w[2 * i] = v.x;
+      st.w[2 * i + 1] = v.y;
+    }
+  }
+}
+
+template <int WT>
+__device__ __forceinline__ void store_stage(Buf& B, const Stage& st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int c = tid + 256 * j;
+    if (c < kRowsM * 9) {
+      const int row = c / 9, part = c - row * 9;
+      const int rt = row >> 5, rl = row & 31;
+      if (part == 0) {
+        const uint32_t h[4] = {st.a[j].x, st.a[j].y, st.a[j].z, st.a[j].w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          B.dx[b][rt][rl] = (uint16_t)(h[b] & 0xffffu);
+          B.sx[rt][rl][b] = (uint16_t)(h[b] >> 16);
+        }
+      } else {
+        *reinterpret_cast<uint4*>(B.aq + row * kStride + (part - 1) * 16) = st.a[j];
+      }
+    }
+  }
+  const int nb = tid >> 1, pair = tid & 1;
+  const int ct = nb >> 5, cl = nb & 31;
+  uint8_t* dst = B.bq + nb * kStride + (2 * pair) * 32;
+  if (WT == 0) {
+    const uint32_t* w = st.w;
     uint32_t q0[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) q0[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], 16);
-    uint8_t* dst = L.b + nb * kBStride + (2 * pair) * 32;
     *reinterpret_cast<uint4*>(dst) = make_uint4(q0[0], q0[1], q0[2], q0[3]);
     *reinterpret_cast<uint4*>(dst + 16) = make_uint4(q0[4], q0[5], q0[6], q0[7]);
     *reinterpret_cast<uint4*>(dst + 32) = make_uint4(w[9], w[10], w[11], w[12]);
     *reinterpret_cast<uint4*>(dst + 48) = make_uint4(w[13], w[14], w[15], w[16]);
-    L.dw[2 * pair][nb] = h2f(w[0] & 0xffffu);
-    L.dw[2 * pair + 1][nb] = h2f(w[8] >> 16);
+    B.dw[2 * pair][ct][cl] = (uint16_t)(w[0] & 0xffffu);
+    B.dw[2 * pair + 1][ct][cl] = (uint16_t)(w[8] >> 16);
   } else {
-    // 128 rows x 4 blocks of 20 bytes = 512 items, two per thread
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int item = tid + it * 256;
-      const int nb = item >> 2, blk = item & 3;
-      const int wrow = epi == 1 ? (nb < 64 ? n0 + nb : n_out + n0 + nb - 64) : n0 + nb;
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(
-          W + (size_t)wrow * row_bytes + (size_t)(stage * kKB + blk) * 20);
-      uint32_t w[5];
-#pragma unroll
-      for (int i = 0; i < 5; ++i) w[i] = src[i];
-      uint8_t* dst = L.b + nb * kBStride + blk * 32;
-      *reinterpret_cast<uint4*>(dst) =
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t* w = st.w + 5 * j;
+      *reinterpret_cast<uint4*>(dst + 32 * j) =
           make_uint4(w[1] & 0x0f0f0f0fu, w[2] & 0x0f0f0f0fu, w[3] & 0x0f0f0f0fu,
                      w[4] & 0x0f0f0f0fu);
-      *reinterpret_cast<uint4*>(dst + 16) =
+      *reinterpret_cast<uint4*>(dst + 32 * j + 16) =
           make_uint4((w[1] >> 4) & 0x0f0f0f0fu, (w[2] >> 4) & 0x0f0f0f0fu,
                      (w[3] >> 4) & 0x0f0f0f0fu, (w[4] >> 4) & 0x0f0f0f0fu);
-      L.dw[blk][nb] = h2f(w[0] & 0xffffu);
-      L.mw[blk][nb] = h2f(w[0] >> 16);
+      B.dw[2 * pair + j][ct][cl] = (uint16_t)(w[0] & 0xffffu);
+      B.mw[ct][cl][2 * pair + j] = (uint16_t)(w[0] >> 16);
     }
   }
 }
 
-__device__ __forceinline__ void stage_acts(Lds& L, const uint8_t* __restrict__ act,
-                                           size_t act_row_bytes, int row0, int nrows, int stage) {
-  for (int c = threadIdx.x; c < kRowsM * 9; c += 256) {
-    const int row = c / 9, part = c - row * 9;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < nrows)
-      v = *reinterpret_cast<const uint4*>(act + (size_t)(row0 + row) * act_row_bytes +
-                                          (size_t)stage * kDs4Bytes + part * 16);
-    *reinterpret_cast<uint4*>(L.a + row * kAStride + part * 16) = v;
-    if (part == 0) {
-      const uint32_t h[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        L.dx[b][row] = h2f(h[b] & 0xffffu);
-        L.sx[b][row] = h2f(h[b] >> 16);
-      }
-    }
-  }
+__device__ __forceinline__ void zero_tables(Buf& B) {
+  // the f16 operands' unused halves (lanes 32..63, k slots 4..7) stay zero for the whole kernel
+  uint32_t* p = reinterpret_cast<uint32_t*>(&B.dx[0][0][0]);
+  const int n = (int)((sizeof(B.dx) + sizeof(B.dw) + sizeof(B.sx) + sizeof(B.mw)) / 4);
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
+__device__ __forceinline__ v8h f16_operand(uint32_t lo) {
+  return __builtin_bit_cast(v8h, (v4i){(int)lo, 0, 0, 0});
 }
 
 template <int WT, int EPI>
-__device__ __forceinline__ void mmq_tile(Lds& L, const MmqProblem& p, const uint8_t* W, int row0,
-                                         int nrows, int ntile) {
+__device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const uint8_t* W,
+                                         int row0, int nrows, int ntile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
@@ -127,81 +173,85 @@ __device__ __forceinline__ void mmq_tile(Lds& L, const MmqProblem& p, const uint
   const size_t row_bytes = (size_t)nblk * block_bytes(WT);
   const size_t act_row_bytes = (size_t)(p.k_in / kDs4Vals) * kDs4Bytes;
   const int n0 = EPI == 1 ? ntile * 64 : ntile * kRowsN;
-  // LDS weight rows of this wavefront's two MFMA tiles
-  const int tb0 = EPI == 1 ? 32 * wc : 64 * wc;
-  const int tb1 = EPI == 1 ? 64 + 32 * wc : 64 * wc + 32;
+  // the wavefront's two column tiles (32 LDS weight rows each)
+  const int ct0 = EPI == 1 ? wc : 2 * wc;
+  const int ct1 = EPI == 1 ? 2 + wc : 2 * wc + 1;
+  const bool live = 32 * wr < nrows;  // a row tile past the expert's rows does no math
 
-  float acc0[16], acc1[16];
+  v16f acc0, acc1;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     acc0[i] = 0.0f;
     acc1[i] = 0.0f;
   }
-  const v16i zero = {0};
+  const v16i izero = {0};
+  const v16f fzero = {0.0f};
   const int nstages = p.k_in / kDs4Vals;
+
+  Stage st;
+  __syncthreads();  // the previous tile's readers are done with both buffers
+  zero_tables(L[0]);
+  zero_tables(L[1]);
+  load_stage<WT>(st, p.act, act_row_bytes, row0, nrows, W, row_bytes, 0, EPI, n0, p.n_out);
+  __syncthreads();
+  store_stage<WT>(L[0], st);
+  __syncthreads();
+
   for (int s = 0; s < nstages; ++s) {
-    __syncthreads();
-    stage_acts(L, p.act, act_row_bytes, row0, nrows, s);
-    stage_weights<WT>(L, W, row_bytes, s, EPI, n0, p.n_out);
-    __syncthreads();
+    if (s + 1 < nstages)
+      load_stage<WT>(st, p.act, act_row_bytes, row0, nrows, W, row_bytes, s + 1, EPI, n0,
+                     p.n_out);
+    const Buf& B = L[s & 1];
+    if (live) {
 #pragma unroll
-    for (int b = 0; b < kKB; ++b) {
-      const v4i a = *reinterpret_cast<const v4i*>(L.a + (32 * wr + l32) * kAStride + 16 + b * 32 +
-                                                  half * 16);
-      const v4i b0 = *reinterpret_cast<const v4i*>(L.b + (tb0 + l32) * kBStride + b * 32 +
-                                                   half * 16);
-      const v4i b1 = *reinterpret_cast<const v4i*>(L.b + (tb1 + l32) * kBStride + b * 32 +
-                                                   half * 16);
-      const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, zero, 0, 0, 0);
-      const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, zero, 0, 0, 0);
-      if (EPI == 2) {
-        int32_t* out = reinterpret_cast<int32_t*>(p.out);
-        const int kb = s * kKB + b;
+      for (int b = 0; b < kKB; ++b) {
+        const v4i a = *reinterpret_cast<const v4i*>(B.aq + (32 * wr + l32) * kStride + b * 32 +
+                                                    half * 16);
+        const v4i b0 = *reinterpret_cast<const v4i*>(B.bq + (32 * ct0 + l32) * kStride +
+                                                     b * 32 + half * 16);
+        const v4i b1 = *reinterpret_cast<const v4i*>(B.bq + (32 * ct1 + l32) * kStride +
+                                                     b * 32 + half * 16);
+        const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
+        const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
+        if (EPI == 2) {
+          int32_t* out = reinterpret_cast<int32_t*>(p.out);
+          const int kb = s * kKB + b;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (row < nrows) {
+              const size_t r = (size_t)(row0 + row);
+              out[(r * p.n_out + n0 + 32 * ct0 + l32) * nblk + kb] = I0[i];
+              out[(r * p.n_out + n0 + 32 * ct1 + l32) * nblk + kb] = I1[i];
+            }
+          }
+          continue;
+        }
+        const v8h sdx = f16_operand(B.dx[b][wr][lane]);
+        const v16f S0 =
+            __builtin_amdgcn_mfma_f32_32x32x16_f16(sdx, f16_operand(B.dw[b][ct0][lane]), fzero,
+                                                    0, 0, 0);
+        const v16f S1 =
+            __builtin_amdgcn_mfma_f32_32x32x16_f16(sdx, f16_operand(B.dw[b][ct1][lane]), fzero,
+                                                    0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (row < nrows) {
-            const size_t r = (size_t)(row0 + row);
-            out[(r * p.n_out + n0 + tb0 + l32) * nblk + kb] = I0[i];
-            out[(r * p.n_out + n0 + tb1 + l32) * nblk + kb] = I1[i];
-          }
+          acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
+          acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
         }
-        continue;
       }
-      const float dw0 = L.dw[b][tb0 + l32];
-      const float dw1 = L.dw[b][tb1 + l32];
-      float dx[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&L.dx[b][32 * wr + 8 * j + 4 * half]);
-        dx[4 * j + 0] = d4.x;
-        dx[4 * j + 1] = d4.y;
-        dx[4 * j + 2] = d4.z;
-        dx[4 * j + 3] = d4.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        acc0[i] = fmaf((float)I0[i], dx[i] * dw0, acc0[i]);
-        acc1[i] = fmaf((float)I1[i], dx[i] * dw1, acc1[i]);
-      }
-      if (WT == 1) {
-        const float mw0 = L.mw[b][tb0 + l32];
-        const float mw1 = L.mw[b][tb1 + l32];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 s4 =
-              *reinterpret_cast<const float4*>(&L.sx[b][32 * wr + 8 * j + 4 * half]);
-          const float sx[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc0[4 * j + q] = fmaf(mw0, sx[q], acc0[4 * j + q]);
-            acc1[4 * j + q] = fmaf(mw1, sx[q], acc1[4 * j + q]);
-          }
-        }
+      if (WT == 1 && EPI != 2) {
+        const v8h sxo = *reinterpret_cast<const v8h*>(&B.sx[wr][lane][0]);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            sxo, *reinterpret_cast<const v8h*>(&B.mw[ct0][lane][0]), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            sxo, *reinterpret_cast<const v8h*>(&B.mw[ct1][lane][0]), acc1, 0, 0, 0);
       }
     }
+    if (s + 1 < nstages) store_stage<WT>(L[(s + 1) & 1], st);
+    __syncthreads();
   }
-  if (EPI == 2) return;
+  if (EPI == 2 || !live) return;
 
   if (EPI == 0) {
     float* out = reinterpret_cast<float*>(p.out);
@@ -210,8 +260,8 @@ __device__ __forceinline__ void mmq_tile(Lds& L, const MmqProblem& p, const uint
       const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
       if (row < nrows) {
         float* o = out + (size_t)(row0 + row) * p.n_out + n0;
-        o[tb0 + l32] = acc0[i];
-        o[tb1 + l32] = acc1[i];
+        o[32 * ct0 + l32] = acc0[i];
+        o[32 * ct1 + l32] = acc1[i];
       }
     }
     return;
@@ -253,7 +303,7 @@ __device__ __forceinline__ void mmq_tile(Lds& L, const MmqProblem& p, const uint
 
 template <int WT, int EPI>
 __global__ __launch_bounds__(256) void mmq_layer_kernel(MmqProblem p) {
-  __shared__ Lds L;
+  __shared__ Buf L[2];
   const int mt = blockIdx.y;
   if (mt >= *p.n_tiles) return;
   const MTile t = p.tiles[mt];
@@ -263,7 +313,7 @@ __global__ __launch_bounds__(256) void mmq_layer_kernel(MmqProblem p) {
 
 template <int WT, int EPI>
 __global__ __launch_bounds__(256) void mmq_group_kernel(MmqProblem p) {
-  __shared__ Lds L;
+  __shared__ Buf L[2];
   const int j = blockIdx.z;
   const int e = p.experts[j];
   const int r0 = p.offsets[e], cnt = p.offsets[e + 1] - r0;

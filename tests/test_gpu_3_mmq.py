@@ -139,3 +139,36 @@ def test_mmq_group_position_independence(orc):
                         dev(q8x), abi.EPI_SWIGLU_Q8_1, out)
         outs.append(host(out))
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+def test_mmq_down_subnormal_scales(orc, wtype):
+    """Activation rows whose q8_1 scales are fp16 subnormals (|h| ~ 1e-3): the scale products
+    must keep them (no flush to zero)."""
+    T, H, F, E, K = 120, 256, 128, 4, 2
+    c, m, _, experts, gbuf = _setup(orc, wtype, T, H, F, E, K, seed=41 + wtype)
+    R = T * K
+    rng = np.random.default_rng(6)
+    h = (rng.standard_normal((R, F)) * 1e-3).astype(np.float32)   # d = amax/127 ~ 2e-5
+    h[::3] *= np.float32(1e-2)
+    hq8 = orc.q8_1_rows(h)
+    _, dx, _ = npref.q8_1_decode(hq8, F)
+    assert np.mean((dx > 0) & (dx < 2.0 ** -14)) > 0.5        # mostly subnormal scales
+    mat_off = 2 * F * (H // 32) * synth.BLOCK_BYTES[wtype]
+    out = torch.zeros((R, H), dtype=torch.float32, device="cuda")
+    note(f"mmq f32 subnormal scales wtype={wtype}")
+    abi.mmq_grouped(wtype, dev(gbuf), c.expert_stride, mat_off, H, F, experts, dev(m["offsets"]),
+                    E, dev(hq8), abi.EPI_F32, out)
+    got = host(out)
+    nb = F // 32
+    for j, e in enumerate(experts):
+        r0, r1 = m["offsets"][e], m["offsets"][e + 1]
+        if r1 == r0:
+            continue
+        wmat = gbuf[j * c.expert_stride + mat_off:j * c.expert_stride + mat_off + H * nb *
+                    synth.BLOCK_BYTES[wtype]]
+        want = orc.mmq_rows(wtype, wmat, H, F, hq8[r0:r1])
+        dots = orc.block_dots(wtype, wmat, H, F, hq8[r0:r1])
+        bound = _abs_term_bound(wtype, wmat, H, F, hq8[r0:r1], dots) * (nb + 2) * 2.0 ** -23
+        assert np.all(np.abs(got[r0:r1] - want) <= bound + 1e-38), (j, e)
+        assert np.count_nonzero(got[r0:r1]) > 0.9 * got[r0:r1].size
