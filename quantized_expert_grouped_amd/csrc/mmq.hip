@@ -27,8 +27,8 @@
 // issued before the current stage's MFMAs and land in the other half of a double-buffered LDS,
 // so each stage costs one barrier.  Weights are unpacked while staging: Q8_0's 34-byte blocks
 // are realigned with v_alignbit, Q4_1's nibbles split into bytes (element j low nibble, j+16
-// high), so both types feed the same int8 MFMA.  Scales stay fp16 bits, laid out in LDS as the
-// f16 MFMA operands (with the unused k slots zero).
+// high), so both types feed the same int8 MFMA.  Scales stay fp16 bits in LDS and become f16
+// MFMA operands directly.
 #include <math.h>
 
 #include "common.hpp"
@@ -51,10 +51,17 @@ constexpr int kStride = 144;      // LDS bytes per row of q: 4 x 32 + 16 of padd
 struct Buf {
   uint8_t aq[kRowsM * kStride];   // activation q, [row][block][32]
   uint8_t bq[kRowsN * kStride];   // weight q as int8, [row][block][32]
-  uint16_t dx[kKB][2][64];        // [block][row tile][lane]: d of row (lane < 32), else 0
-  uint16_t dw[kKB][4][64];        // [block][col tile][lane]: d of weight row, else 0
-  uint16_t sx[2][64][8];          // [row tile][lane][k]: s of the stage's 4 blocks, rest 0
-  uint16_t mw[4][64][8];          // [col tile][lane][k]: m of the stage's 4 blocks, rest 0
+  uint16_t dx[kKB][2][32];        // [block][row tile][row]: fp16 d of the activation rows
+  uint16_t dw[kKB][4][32];        // [block][col tile][row]: fp16 d of the weight rows
+  uint32_t sx[kRowsM][2];         // [row][pair]: fp16 s of blocks (2p, 2p+1)
+  uint32_t mw[kRowsN][2];         // [weight row][pair]: fp16 m of blocks (2p, 2p+1)
+};
+
+// The upper 32 lanes feed zeros into the single-k f16 outer products; they read them from
+// this shadow, which has the layout of Buf::dx / Buf::dw and stays zero.
+struct Zeros {
+  uint16_t dx[kKB][2][32];
+  uint16_t dw[kKB][4][32];
 };
 
 struct Stage {  // one thread's share of a stage's global loads, held in registers
@@ -113,10 +120,9 @@ __device__ __forceinline__ void store_stage(Buf& B, const Stage& st) {
       if (part == 0) {
         const uint32_t h[4] = {st.a[j].x, st.a[j].y, st.a[j].z, st.a[j].w};
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          B.dx[b][rt][rl] = (uint16_t)(h[b] & 0xffffu);
-          B.sx[rt][rl][b] = (uint16_t)(h[b] >> 16);
-        }
+        for (int b = 0; b < 4; ++b) B.dx[b][rt][rl] = (uint16_t)(h[b] & 0xffffu);
+        B.sx[row][0] = (h[0] >> 16) | (h[1] & 0xffff0000u);
+        B.sx[row][1] = (h[2] >> 16) | (h[3] & 0xffff0000u);
       } else {
         *reinterpret_cast<uint4*>(B.aq + row * kStride + (part - 1) * 16) = st.a[j];
       }
@@ -137,6 +143,7 @@ __device__ __forceinline__ void store_stage(Buf& B, const Stage& st) {
     B.dw[2 * pair][ct][cl] = (uint16_t)(w[0] & 0xffffu);
     B.dw[2 * pair + 1][ct][cl] = (uint16_t)(w[8] >> 16);
   } else {
+    B.mw[nb][pair] = (st.w[0] >> 16) | (st.w[5] & 0xffff0000u);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t* w = st.w + 5 * j;
@@ -147,25 +154,18 @@ __device__ __forceinline__ void store_stage(Buf& B, const Stage& st) {
           make_uint4((w[1] >> 4) & 0x0f0f0f0fu, (w[2] >> 4) & 0x0f0f0f0fu,
                      (w[3] >> 4) & 0x0f0f0f0fu, (w[4] >> 4) & 0x0f0f0f0fu);
       B.dw[2 * pair + j][ct][cl] = (uint16_t)(w[0] & 0xffffu);
-      B.mw[ct][cl][2 * pair + j] = (uint16_t)(w[0] >> 16);
     }
   }
 }
 
-__device__ __forceinline__ void zero_tables(Buf& B) {
-  // the f16 operands' unused halves (lanes 32..63, k slots 4..7) stay zero for the whole kernel
-  uint32_t* p = reinterpret_cast<uint32_t*>(&B.dx[0][0][0]);
-  const int n = (int)((sizeof(B.dx) + sizeof(B.dw) + sizeof(B.sx) + sizeof(B.mw)) / 4);
-  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
-}
-
-__device__ __forceinline__ v8h f16_operand(uint32_t lo) {
-  return __builtin_bit_cast(v8h, (v4i){(int)lo, 0, 0, 0});
+__device__ __forceinline__ void zero_shadow(Zeros& Z) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(&Z);
+  for (int i = threadIdx.x; i < (int)(sizeof(Zeros) / 4); i += 256) p[i] = 0u;
 }
 
 template <int WT, int EPI>
-__device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const uint8_t* W,
-                                         int row0, int nrows, int ntile) {
+__device__ __forceinline__ void mmq_tile(Buf (&L)[2], const Zeros& Z, const MmqProblem& p,
+                                         const uint8_t* W, int row0, int nrows, int ntile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
@@ -188,12 +188,12 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const
   const v16f fzero = {0.0f};
   const int nstages = p.k_in / kDs4Vals;
 
+  // f16 MFMA operands: element 0 carries the value, the other three dwords stay zero
+  v4i op_dx = {0, 0, 0, 0}, op_dw0 = {0, 0, 0, 0}, op_dw1 = {0, 0, 0, 0};
+
   Stage st;
-  __syncthreads();  // the previous tile's readers are done with both buffers
-  zero_tables(L[0]);
-  zero_tables(L[1]);
   load_stage<WT>(st, p.act, act_row_bytes, row0, nrows, W, row_bytes, 0, EPI, n0, p.n_out);
-  __syncthreads();
+  __syncthreads();  // the previous tile's readers are done with both buffers
   store_stage<WT>(L[0], st);
   __syncthreads();
 
@@ -203,18 +203,18 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const
                      p.n_out);
     const Buf& B = L[s & 1];
     if (live) {
+      const uint8_t* arow = B.aq + (32 * wr + l32) * kStride + half * 16;
+      const uint8_t* brow0 = B.bq + (32 * ct0 + l32) * kStride + half * 16;
+      const uint8_t* brow1 = B.bq + (32 * ct1 + l32) * kStride + half * 16;
+      if (EPI == 2) {
+        int32_t* out = reinterpret_cast<int32_t*>(p.out);
 #pragma unroll
-      for (int b = 0; b < kKB; ++b) {
-        const v4i a = *reinterpret_cast<const v4i*>(B.aq + (32 * wr + l32) * kStride + b * 32 +
-                                                    half * 16);
-        const v4i b0 = *reinterpret_cast<const v4i*>(B.bq + (32 * ct0 + l32) * kStride +
-                                                     b * 32 + half * 16);
-        const v4i b1 = *reinterpret_cast<const v4i*>(B.bq + (32 * ct1 + l32) * kStride +
-                                                     b * 32 + half * 16);
-        const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
-        const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
-        if (EPI == 2) {
-          int32_t* out = reinterpret_cast<int32_t*>(p.out);
+        for (int b = 0; b < kKB; ++b) {
+          const v4i a = *reinterpret_cast<const v4i*>(arow + b * 32);
+          const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              a, *reinterpret_cast<const v4i*>(brow0 + b * 32), izero, 0, 0, 0);
+          const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              a, *reinterpret_cast<const v4i*>(brow1 + b * 32), izero, 0, 0, 0);
           const int kb = s * kKB + b;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -225,27 +225,54 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const
               out[(r * p.n_out + n0 + 32 * ct1 + l32) * nblk + kb] = I1[i];
             }
           }
-          continue;
         }
-        const v8h sdx = f16_operand(B.dx[b][wr][lane]);
-        const v16f S0 =
-            __builtin_amdgcn_mfma_f32_32x32x16_f16(sdx, f16_operand(B.dw[b][ct0][lane]), fzero,
-                                                    0, 0, 0);
-        const v16f S1 =
-            __builtin_amdgcn_mfma_f32_32x32x16_f16(sdx, f16_operand(B.dw[b][ct1][lane]), fzero,
-                                                    0, 0, 0);
+      } else {
+        // f16 outer-product operands: the lower 32 lanes carry this stage's d values in k slot 0,
+        // the upper 32 lanes read the zero shadow
+        const uint16_t* dxp = half ? &Z.dx[0][wr][l32] : &B.dx[0][wr][l32];
+        const uint16_t* dwp0 = half ? &Z.dw[0][ct0][l32] : &B.dw[0][ct0][l32];
+        const uint16_t* dwp1 = half ? &Z.dw[0][ct1][l32] : &B.dw[0][ct1][l32];
+        constexpr int kDxB = 2 * 32, kDwB = 4 * 32;  // element strides between blocks
+        v16i I0, I1;
+        v16f S0, S1;
+        auto issue = [&](int b) {
+          const v4i a = *reinterpret_cast<const v4i*>(arow + b * 32);
+          I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              a, *reinterpret_cast<const v4i*>(brow0 + b * 32), izero, 0, 0, 0);
+          I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              a, *reinterpret_cast<const v4i*>(brow1 + b * 32), izero, 0, 0, 0);
+          op_dx[0] = dxp[b * kDxB];
+          op_dw0[0] = dwp0[b * kDwB];
+          op_dw1[0] = dwp1[b * kDwB];
+          const v8h sdx = __builtin_bit_cast(v8h, op_dx);
+          S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              sdx, __builtin_bit_cast(v8h, op_dw0), fzero, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              sdx, __builtin_bit_cast(v8h, op_dw1), fzero, 0, 0, 0);
+        };
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
-          acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
+        for (int b = 0; b < kKB; ++b) {
+          // (issuing the next block's MFMAs ahead of this block's VALU needs ~290 registers and
+          // halves the occupancy; two resident wavefronts per SIMD interleave instead)
+          issue(b);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
+            acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
+          }
         }
-      }
-      if (WT == 1 && EPI != 2) {
-        const v8h sxo = *reinterpret_cast<const v8h*>(&B.sx[wr][lane][0]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            sxo, *reinterpret_cast<const v8h*>(&B.mw[ct0][lane][0]), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            sxo, *reinterpret_cast<const v8h*>(&B.mw[ct1][lane][0]), acc1, 0, 0, 0);
+        if (WT == 1) {
+          // sum over the stage's 4 blocks of mw * sx: lanes 0..31 carry blocks 0,1 and lanes
+          // 32..63 blocks 2,3 of the same rows, so no k slot is wasted on zeros
+          op_dx[0] = (int)B.sx[32 * wr + l32][half];
+          op_dw0[0] = (int)B.mw[32 * ct0 + l32][half];
+          op_dw1[0] = (int)B.mw[32 * ct1 + l32][half];
+          const v8h sxo = __builtin_bit_cast(v8h, op_dx);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxo, __builtin_bit_cast(v8h, op_dw0),
+                                                        acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxo, __builtin_bit_cast(v8h, op_dw1),
+                                                        acc1, 0, 0, 0);
+        }
       }
     }
     if (s + 1 < nstages) store_stage<WT>(L[(s + 1) & 1], st);
@@ -267,7 +294,9 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const
     return;
   }
 
-  // EPI == 1: h = silu(g) * u, then q8_1 along F: the 32 lanes of a half hold one block
+  // EPI == 1: h = silu(g) * u, then q8_1 along F: the 32 lanes of a half hold one block.
+  // silu uses the hardware exp and reciprocal (h only has to be accurate); the quantisation of
+  // h is the exact q8_1 arithmetic.
   const int f = n0 + 32 * wc + l32;
   const int fb = (n0 + 32 * wc) / kQK;  // block index along F
   const size_t h_row_bytes = (size_t)(p.n_out / kDs4Vals) * kDs4Bytes;
@@ -278,7 +307,7 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const
   for (int i = 0; i < 16; ++i) {
     const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
     const float g = acc0[i], u = acc1[i];
-    const float h = g / (1.0f + expf(-g)) * u;
+    const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
     float am = fabsf(h);
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
@@ -304,22 +333,27 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const MmqProblem& p, const
 template <int WT, int EPI>
 __global__ __launch_bounds__(256) void mmq_layer_kernel(MmqProblem p) {
   __shared__ Buf L[2];
+  __shared__ Zeros Z;
   const int mt = blockIdx.y;
   if (mt >= *p.n_tiles) return;
+  zero_shadow(Z);
   const MTile t = p.tiles[mt];
   const uint8_t* W = p.wbase + (size_t)t.ordinal * p.pos_stride + p.mat_offset;
-  mmq_tile<WT, EPI>(L, p, W, t.row0, t.nrows, blockIdx.x);
+  mmq_tile<WT, EPI>(L, Z, p, W, t.row0, t.nrows, blockIdx.x);
 }
 
 template <int WT, int EPI>
 __global__ __launch_bounds__(256) void mmq_group_kernel(MmqProblem p) {
   __shared__ Buf L[2];
+  __shared__ Zeros Z;
+  zero_shadow(Z);
   const int j = blockIdx.z;
   const int e = p.experts[j];
   const int r0 = p.offsets[e], cnt = p.offsets[e + 1] - r0;
   const uint8_t* W = p.wbase + (size_t)j * p.pos_stride + p.mat_offset;
   for (int m = blockIdx.y; m * kRowsM < cnt; m += gridDim.y)
-    mmq_tile<WT, EPI>(L, p, W, r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM), blockIdx.x);
+    mmq_tile<WT, EPI>(L, Z, p, W, r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM),
+                      blockIdx.x);
 }
 
 template <int WT, int EPI>
