@@ -15,6 +15,7 @@ CPU baseline times the plain C oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -66,6 +67,58 @@ def algorithmic_work(c, n_active: int):
     }
 
 
+KERNEL_SOURCES = ("quantized_expert_grouped_amd/csrc/mmq.hip",
+                  "quantized_expert_grouped_amd/csrc/common.hpp",
+                  "quantized_expert_grouped_amd/csrc/internal.hpp")
+STAGE_KERNEL = {"gate_up": "mmq_gate_up", "down": "mmq_down"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM-side bytes per launch of a stage's kernel from the committed counter summary
+    (profiles/<kernel>_<workload>_traffic.txt), or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    kern = STAGE_KERNEL.get(stage)
+    if kern is None:
+        return None
+    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib: int, dev) -> None:
+    """One plain device-to-device copy of a known size, launched before the steps so that a
+    counter run over this program also measures a kernel whose traffic is known (the
+    calibration of FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(c, idx, w, target_s: float = 12.0):
     """Time the oracle (as it stands) on the first tokens of the same workload."""
     import oracle
@@ -98,6 +151,9 @@ def main():
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the steps without the per-stage events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain copy of this many MiB before the steps (counter "
+                         "calibration; outside the timed region)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -118,6 +174,8 @@ def main():
     logits = torch.from_numpy(c.logits).to(dev)
     out = torch.empty((c.T, c.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib, dev)
 
     for _ in range(args.warmup):
         layer.step(x, logits, out)
@@ -174,12 +232,14 @@ def main():
             achieved = amt / t_s / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                         "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
-                        "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": None}
+                        "frac": round(achieved / PEAK_I8_TOPS, 4),
+                        "traffic": measured_traffic(dom, c.name)}
         else:
             achieved = amt / t_s / 1e9
             roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+                        "frac": round(achieved / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic(dom, c.name)}
 
     cpu = None
     if not args.no_cpu_baseline:

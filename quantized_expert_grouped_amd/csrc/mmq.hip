@@ -7,15 +7,18 @@
 // For weight row n and activation row r, block b (32 values):
 //   I_b = sum_j qw_j * qx_j                 exact int32: one v_mfma_i32_32x32x32_i8 per block
 //                                           (K = 32 is exactly one block)
-//   S_b = dx_b * dw_b                       exact in fp32 (two fp16 significands): for a whole
-//                                           32x32 tile this is an outer product, one
-//                                           v_mfma_f32_32x32x16_f16 with a single nonzero k
+//   S_b = dx_b * dw_b                       exact in fp32 (two fp16 significands); for a whole
+//                                           32x32 tile an outer product: one
+//                                           v_mfma_f32_32x32x16_f16
 //   acc = fma(float(I_b), S_b, acc)         the only per-element VALU work (convert + fma)
 //   Q4_1 adds sum_b mw_b * sx_b             a true sum over blocks: an f16 MFMA whose C input
 //                                           is the accumulator itself
-// Blocks are taken in ascending order and every output element is accumulated by one lane in
-// one fixed instruction sequence, so results do not depend on the tiling, the group size, the
-// ring start or the row's place in its tile.
+// Both halves of the wavefront feed the same scale into the f16 MFMAs (no zero lanes), so they
+// produce exactly 2*S_b and 2*sum(mw*sx); the accumulator carries that factor 2 and is halved
+// once at the end, which in binary floating point changes no rounding.  Blocks are taken in
+// ascending order and every output element is accumulated by one lane in one fixed instruction
+// sequence, so results do not depend on the tiling, the group size, the ring start or the row's
+// place in its tile.
 //
 // Workgroup: 64 activation rows (one m-tile of one expert) x 128 weight rows, 4 wavefronts.
 // Wavefront (wr, wc) owns rows 32*wr.. and two 32-row column tiles of the weights:
@@ -23,12 +26,13 @@
 //     h = silu(g) * u is formed in registers and requantised along F across the 32 lanes that
 //     hold one block of 32 features;
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
-// K loop: stages of 4 blocks (128 values, one q8_1 group).  The next stage's global loads are
-// issued before the current stage's MFMAs and land in the other half of a double-buffered LDS,
-// so each stage costs one barrier.  Weights are unpacked while staging: Q8_0's 34-byte blocks
-// are realigned with v_alignbit, Q4_1's nibbles split into bytes (element j low nibble, j+16
-// high), so both types feed the same int8 MFMA.  Scales stay fp16 bits in LDS and become f16
-// MFMA operands directly.
+// K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of LDS
+// buffers with direct global->LDS loads (global_load_lds_dwordx4; 4-byte pieces for Q8_0, whose
+// 34-byte blocks leave rows only 8-byte aligned), two stages ahead of the MFMAs (a ring of three), so the
+// registers hold no staged data and no VALU moves it.  Fragments are read from the raw bytes:
+// q8_1 rows keep their 144-byte groups, Q8_0 blocks are realigned with v_alignbit, Q4_1 nibbles
+// are split with two masks: a lane half h takes elements 8h..8h+7 and 16+8h..16+8h+7 of a block
+// (8 packed bytes), on both operands, so the int8 dot product is unchanged.
 #include <math.h>
 
 #include "common.hpp"
@@ -42,31 +46,27 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 constexpr int kRowsM = kMmqRows;  // 64 activation rows per workgroup
 constexpr int kRowsN = 128;       // weight rows per workgroup
 constexpr int kKB = 4;            // blocks per stage
-constexpr int kStride = 144;      // LDS bytes per row of q: 4 x 32 + 16 of padding
+constexpr int kARow = 144;        // bytes of one q8_1 group (the stage's slice of a row)
+constexpr int kAInstr = kRowsM * kARow / (64 * 16);  // 9 DMA instructions per stage
 
-struct Buf {
-  uint8_t aq[kRowsM * kStride];   // activation q, [row][block][32]
-  uint8_t bq[kRowsN * kStride];   // weight q as int8, [row][block][32]
-  uint16_t dx[kKB][2][32];        // [block][row tile][row]: fp16 d of the activation rows
-  uint16_t dw[kKB][4][32];        // [block][col tile][row]: fp16 d of the weight rows
-  uint32_t sx[kRowsM][2];         // [row][pair]: fp16 s of blocks (2p, 2p+1)
-  uint32_t mw[kRowsN][2];         // [weight row][pair]: fp16 m of blocks (2p, 2p+1)
+template <int WT>
+struct Geo {
+  static constexpr int kBRow = WT == 0 ? 4 * 34 : 4 * 20;  // raw bytes of a row per stage
+  static constexpr int kBChunk = WT == 0 ? 4 : 16;         // bytes per lane per DMA
+  static constexpr int kBInstr = kRowsN * kBRow / (64 * kBChunk);  // 68 or 10
+  static constexpr int kBPerWave = (kBInstr + 3) / 4;              // 17 or 3
 };
 
-// The upper 32 lanes feed zeros into the single-k f16 outer products; they read them from
-// this shadow, which has the layout of Buf::dx / Buf::dw and stays zero.
-struct Zeros {
-  uint16_t dx[kKB][2][32];
-  uint16_t dw[kKB][4][32];
-};
-
-struct Stage {  // one thread's share of a stage's global loads, held in registers
-  uint4 a[3];
-  uint32_t w[17];
+template <int WT>
+struct alignas(16) StageBuf {
+  uint8_t a[kRowsM * kARow];
+  uint8_t b[kRowsN * Geo<WT>::kBRow];
 };
 
 __device__ __forceinline__ int weight_row(int epi, int nb, int n0, int n_out) {
@@ -74,98 +74,155 @@ __device__ __forceinline__ int weight_row(int epi, int nb, int n0, int n_out) {
   return epi == 1 ? (nb < 64 ? n0 + nb : n_out + n0 + nb - 64) : n0 + nb;
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (n is wave-uniform, at most 20 here)
+__device__ __forceinline__ void wait_vm(int n) {
+#define MOE_VM(k) \
+  case k:         \
+    __builtin_amdgcn_s_waitcnt(((k)&0xF) | (((k) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); \
+    break;
+  switch (n) {
+    MOE_VM(0) MOE_VM(1) MOE_VM(2) MOE_VM(3) MOE_VM(4) MOE_VM(5) MOE_VM(6) MOE_VM(7) MOE_VM(8)
+    MOE_VM(9) MOE_VM(10) MOE_VM(11) MOE_VM(12) MOE_VM(13) MOE_VM(14) MOE_VM(15) MOE_VM(16)
+    MOE_VM(17) MOE_VM(18) MOE_VM(19) MOE_VM(20)
+    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;  // vmcnt(0)
+  }
+#undef MOE_VM
+}
+
+// Each lane's byte offsets of its DMA pieces, relative to the stage's first byte in global
+// memory; fixed for a tile, the stage advance is added to the (uniform) base pointer.
 template <int WT>
-__device__ __forceinline__ void load_stage(Stage& st, const uint8_t* __restrict__ act,
-                                           size_t act_row_bytes, int row0, int nrows,
-                                           const uint8_t* __restrict__ W, size_t row_bytes,
-                                           int s, int epi, int n0, int n_out) {
-  const int tid = threadIdx.x;
+struct DmaPlan {
+  uint32_t a[3];
+  uint32_t b[Geo<WT>::kBPerWave];
+};
+
+__device__ __forceinline__ int wave_id() {  // uniform across the wavefront, kept in an SGPR
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+template <int WT>
+__device__ __forceinline__ void plan_dma(DmaPlan<WT>& d, size_t act_row_bytes, int nrows,
+                                         size_t row_bytes, int epi, int n0, int n_out) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const int c = tid + 256 * j;  // 64 rows x 9 chunks of 16 bytes
-    const int row = c / 9, part = c - row * 9;
-    st.a[j] = make_uint4(0u, 0u, 0u, 0u);
-    if (c < kRowsM * 9 && row < nrows)
-      st.a[j] = *reinterpret_cast<const uint4*>(act + (size_t)(row0 + row) * act_row_bytes +
-                                                (size_t)s * kDs4Bytes + part * 16);
+    const int c = 64 * (wave + 4 * j) + lane;  // 16-byte piece of the 64 x 144-byte slice
+    const int row = min(c / 9, nrows - 1);     // rows past the expert repeat its last row
+    d.a[j] = (uint32_t)(row * act_row_bytes + (c % 9) * 16);
   }
-  const int nb = tid >> 1, pair = tid & 1;  // 128 weight rows x 2 pairs of blocks
-  const uint8_t* src = W + (size_t)weight_row(epi, nb, n0, n_out) * row_bytes;
-  if (WT == 0) {
-    const uint32_t* p =
-        reinterpret_cast<const uint32_t*>(src + (size_t)s * (kKB * 34) + pair * 68);
 #pragma unroll
-    for (int i = 0; i < 17; ++i) st.w[i] = p[i];
-  } else {
-    const uint2* p =
-        reinterpret_cast<const uint2*>(src + (size_t)(s * kKB + 2 * pair) * 20);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const uint2 v = p[i];
-      st.w[2 * i] = v.x;
-      st.w[2 * i + 1] = v.y;
+  for (int j = 0; j < Geo<WT>::kBPerWave; ++j) {
+    const int c = 64 * (wave + 4 * j) + lane;
+    if (WT == 0) {
+      const int row = c / 34;  // 34 dwords of a row's 4 blocks
+      d.b[j] = (uint32_t)(weight_row(epi, min(row, kRowsN - 1), n0, n_out) * row_bytes +
+                          (c % 34) * 4);
+    } else {
+      const int row = c / 5;  // 5 pieces of a row's 4 blocks
+      d.b[j] = (uint32_t)(weight_row(epi, min(row, kRowsN - 1), n0, n_out) * row_bytes +
+                          (c % 5) * 16);
     }
   }
 }
 
 template <int WT>
-__device__ __forceinline__ void store_stage(Buf& B, const Stage& st) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ int dma_count() {  // DMA instructions this wavefront issues per stage
+  const int wave = wave_id();
+  const int na = (kAInstr - wave + 3) / 4;
+  const int nb = (Geo<WT>::kBInstr - wave + 3) / 4;
+  return na + nb;
+}
+
+// One direct global->LDS load: lane i's 16 (or 4) bytes land at lds + 16*i (4*i), lds
+// wave-uniform (it is passed in M0).  Written as inline assembly so that the compiler's wait-count
+// pass does not treat every later LDS read as possibly overlapping it (it cannot tell the ring
+// buffers apart and would drain the loads in flight); the kernel orders these loads itself with
+// explicit vmcnt waits and barriers.  Every other VMEM operation of the kernel retires in issue
+// order with these, so the compiler's own waits stay correct (they can only wait longer).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// M0 is an input operand (the compiler writes it); the s_nop covers the one wait state an LDS
+// DMA needs after an M0 write.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "{m0}"(lds), "v"(g) : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %1, off" : : "{m0}"(lds), "v"(g) : "memory");
+}
+
+template <int WT>
+__device__ __forceinline__ void issue_stage(StageBuf<WT>& S, const DmaPlan<WT>& d,
+                                            const uint8_t* abase, const uint8_t* wbase) {
+  const int wave = wave_id();
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const int c = tid + 256 * j;
-    if (c < kRowsM * 9) {
-      const int row = c / 9, part = c - row * 9;
-      const int rt = row >> 5, rl = row & 31;
-      if (part == 0) {
-        const uint32_t h[4] = {st.a[j].x, st.a[j].y, st.a[j].z, st.a[j].w};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) B.dx[b][rt][rl] = (uint16_t)(h[b] & 0xffffu);
-        B.sx[row][0] = (h[0] >> 16) | (h[1] & 0xffff0000u);
-        B.sx[row][1] = (h[2] >> 16) | (h[3] & 0xffff0000u);
-      } else {
-        *reinterpret_cast<uint4*>(B.aq + row * kStride + (part - 1) * 16) = st.a[j];
-      }
-    }
+    const int i = wave + 4 * j;
+    if (i < kAInstr) dma16(abase + d.a[j], lds_address(S.a + i * 1024));
   }
-  const int nb = tid >> 1, pair = tid & 1;
-  const int ct = nb >> 5, cl = nb & 31;
-  uint8_t* dst = B.bq + nb * kStride + (2 * pair) * 32;
-  if (WT == 0) {
-    const uint32_t* w = st.w;
-    uint32_t q0[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q0[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], 16);
-    *reinterpret_cast<uint4*>(dst) = make_uint4(q0[0], q0[1], q0[2], q0[3]);
-    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(q0[4], q0[5], q0[6], q0[7]);
-    *reinterpret_cast<uint4*>(dst + 32) = make_uint4(w[9], w[10], w[11], w[12]);
-    *reinterpret_cast<uint4*>(dst + 48) = make_uint4(w[13], w[14], w[15], w[16]);
-    B.dw[2 * pair][ct][cl] = (uint16_t)(w[0] & 0xffffu);
-    B.dw[2 * pair + 1][ct][cl] = (uint16_t)(w[8] >> 16);
-  } else {
-    B.mw[nb][pair] = (st.w[0] >> 16) | (st.w[5] & 0xffff0000u);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t* w = st.w + 5 * j;
-      *reinterpret_cast<uint4*>(dst + 32 * j) =
-          make_uint4(w[1] & 0x0f0f0f0fu, w[2] & 0x0f0f0f0fu, w[3] & 0x0f0f0f0fu,
-                     w[4] & 0x0f0f0f0fu);
-      *reinterpret_cast<uint4*>(dst + 32 * j + 16) =
-          make_uint4((w[1] >> 4) & 0x0f0f0f0fu, (w[2] >> 4) & 0x0f0f0f0fu,
-                     (w[3] >> 4) & 0x0f0f0f0fu, (w[4] >> 4) & 0x0f0f0f0fu);
-      B.dw[2 * pair + j][ct][cl] = (uint16_t)(w[0] & 0xffffu);
+  for (int j = 0; j < Geo<WT>::kBPerWave; ++j) {
+    const int i = wave + 4 * j;
+    if (i < Geo<WT>::kBInstr) {
+      if (WT == 0)
+        dma4(wbase + d.b[j], lds_address(S.b + i * 64 * 4));
+      else
+        dma16(wbase + d.b[j], lds_address(S.b + i * 64 * 16));
     }
   }
 }
 
-__device__ __forceinline__ void zero_shadow(Zeros& Z) {
-  uint32_t* p = reinterpret_cast<uint32_t*>(&Z);
-  for (int i = threadIdx.x; i < (int)(sizeof(Zeros) / 4); i += 256) p[i] = 0u;
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// int8 MFMA operands of block b.  Q4_1: lane half h takes elements 8h..8h+7, 16+8h..16+8h+7.
+// Q8_0: lane half h takes elements 16h..16h+15.
+template <int WT>
+__device__ __forceinline__ v4i a_frag(const uint8_t* arow, int b, int half) {
+  const uint8_t* q = arow + 16 + 32 * b;
+  if (WT == 1) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(q + 8 * half);
+    const uint2 hi = *reinterpret_cast<const uint2*>(q + 16 + 8 * half);
+    return (v4i){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+  }
+  return *reinterpret_cast<const v4i*>(q + 16 * half);
+}
+
+template <int WT>
+__device__ __forceinline__ v4i b_frag(const uint8_t* brow, int b, int half) {
+  if (WT == 1) {
+    const uint8_t* q = brow + 20 * b + 4 + 8 * half;  // 4-byte aligned
+    const uint32_t x0 = lds_u32(q), x1 = lds_u32(q + 4);
+    const uint32_t m = 0x0f0f0f0fu;
+    return (v4i){(int)(x0 & m), (int)(x1 & m), (int)((x0 >> 4) & m), (int)((x1 >> 4) & m)};
+  }
+  if ((b & 1) == 0) {  // q of an even block starts 2 bytes past a 4-byte boundary
+    const uint8_t* p = brow + 34 * b + 16 * half;
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) w[i] = lds_u32(p + 4 * i);
+    return (v4i){(int)__builtin_amdgcn_alignbit(w[1], w[0], 16),
+                 (int)__builtin_amdgcn_alignbit(w[2], w[1], 16),
+                 (int)__builtin_amdgcn_alignbit(w[3], w[2], 16),
+                 (int)__builtin_amdgcn_alignbit(w[4], w[3], 16)};
+  }
+  const uint8_t* p = brow + 34 * b + 2 + 16 * half;
+  return (v4i){(int)lds_u32(p), (int)lds_u32(p + 4), (int)lds_u32(p + 8), (int)lds_u32(p + 12)};
+}
+
+template <int WT>
+__device__ __forceinline__ uint32_t b_scale(const uint8_t* brow, int b) {  // fp16 d, zero-extended
+  return *reinterpret_cast<const uint16_t*>(brow + (WT == 1 ? 20 : 34) * b);
 }
 
 template <int WT, int EPI>
-__device__ __forceinline__ void mmq_tile(Buf (&L)[2], const Zeros& Z, const MmqProblem& p,
-                                         const uint8_t* W, int row0, int nrows, int ntile) {
+__device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, StageBuf<WT>& L2,
+                                         const MmqProblem& p, const uint8_t* W, int row0,
+                                         int nrows, int ntile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
@@ -177,6 +234,12 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const Zeros& Z, const MmqP
   const int ct0 = EPI == 1 ? wc : 2 * wc;
   const int ct1 = EPI == 1 ? 2 + wc : 2 * wc + 1;
   const bool live = 32 * wr < nrows;  // a row tile past the expert's rows does no math
+  const int nstages = p.k_in / kDs4Vals;
+  const uint8_t* abase = p.act + (size_t)row0 * act_row_bytes;
+
+  DmaPlan<WT> plan;
+  plan_dma<WT>(plan, act_row_bytes, nrows, row_bytes, EPI, n0, p.n_out);
+  const int per_stage = dma_count<WT>();
 
   v16f acc0, acc1;
 #pragma unroll
@@ -186,99 +249,103 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const Zeros& Z, const MmqP
   }
   const v16i izero = {0};
   const v16f fzero = {0.0f};
-  const int nstages = p.k_in / kDs4Vals;
+  // f16 operands: dword 0 carries the fp16 value(s), the other dwords stay zero
+  v4i op_x = {0, 0, 0, 0}, op_w0 = {0, 0, 0, 0}, op_w1 = {0, 0, 0, 0};
 
-  // f16 MFMA operands: element 0 carries the value, the other three dwords stay zero
-  v4i op_dx = {0, 0, 0, 0}, op_dw0 = {0, 0, 0, 0}, op_dw1 = {0, 0, 0, 0};
+  auto issue = [&](StageBuf<WT>& buf, int t) {
+    issue_stage<WT>(buf, plan, abase + (size_t)t * kARow, W + (size_t)t * Geo<WT>::kBRow);
+  };
 
-  Stage st;
-  load_stage<WT>(st, p.act, act_row_bytes, row0, nrows, W, row_bytes, 0, EPI, n0, p.n_out);
-  __syncthreads();  // the previous tile's readers are done with both buffers
-  store_stage<WT>(L[0], st);
-  __syncthreads();
-
-  for (int s = 0; s < nstages; ++s) {
-    if (s + 1 < nstages)
-      load_stage<WT>(st, p.act, act_row_bytes, row0, nrows, W, row_bytes, s + 1, EPI, n0,
-                     p.n_out);
-    const Buf& B = L[s & 1];
-    if (live) {
-      const uint8_t* arow = B.aq + (32 * wr + l32) * kStride + half * 16;
-      const uint8_t* brow0 = B.bq + (32 * ct0 + l32) * kStride + half * 16;
-      const uint8_t* brow1 = B.bq + (32 * ct1 + l32) * kStride + half * 16;
-      if (EPI == 2) {
-        int32_t* out = reinterpret_cast<int32_t*>(p.out);
+  // One stage: wait until stage s is in LDS for every wave (which also means every wave is done
+  // with stage s-1, whose buffer `fill` then receives stage s+2), then its MFMAs.  The three
+  // buffers are distinct LDS objects used with fixed roles per unrolled step, so the compiler
+  // can tell the reads of one from the loads into another and keeps the loads in flight.
+  auto step = [&](int s, const StageBuf<WT>& cur, StageBuf<WT>& fill) {
+    // (the raw block-dot epilogue also stores inside the loop, so it drains the counter)
+    const int ahead = EPI == 2 ? 0 : min(1, nstages - 1 - s);
+    wait_vm(ahead * per_stage);
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < nstages) issue(fill, s + 2);
+    if (!live) return;
+    const uint8_t* arow = cur.a + (32 * wr + l32) * kARow;
+    const uint8_t* brow0 = cur.b + (32 * ct0 + l32) * Geo<WT>::kBRow;
+    const uint8_t* brow1 = cur.b + (32 * ct1 + l32) * Geo<WT>::kBRow;
+    if (EPI == 2) {
+      int32_t* out = reinterpret_cast<int32_t*>(p.out);
 #pragma unroll
-        for (int b = 0; b < kKB; ++b) {
-          const v4i a = *reinterpret_cast<const v4i*>(arow + b * 32);
-          const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-              a, *reinterpret_cast<const v4i*>(brow0 + b * 32), izero, 0, 0, 0);
-          const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-              a, *reinterpret_cast<const v4i*>(brow1 + b * 32), izero, 0, 0, 0);
-          const int kb = s * kKB + b;
+      for (int b = 0; b < kKB; ++b) {
+        const v4i a = a_frag<WT>(arow, b, half);
+        const v16i I0 =
+            __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow0, b, half), izero, 0, 0, 0);
+        const v16i I1 =
+            __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow1, b, half), izero, 0, 0, 0);
+        const int kb = s * kKB + b;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (row < nrows) {
-              const size_t r = (size_t)(row0 + row);
-              out[(r * p.n_out + n0 + 32 * ct0 + l32) * nblk + kb] = I0[i];
-              out[(r * p.n_out + n0 + 32 * ct1 + l32) * nblk + kb] = I1[i];
-            }
+        for (int i = 0; i < 16; ++i) {
+          const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (row < nrows) {
+            const size_t r = (size_t)(row0 + row);
+            out[(r * p.n_out + n0 + 32 * ct0 + l32) * nblk + kb] = I0[i];
+            out[(r * p.n_out + n0 + 32 * ct1 + l32) * nblk + kb] = I1[i];
           }
-        }
-      } else {
-        // f16 outer-product operands: the lower 32 lanes carry this stage's d values in k slot 0,
-        // the upper 32 lanes read the zero shadow
-        const uint16_t* dxp = half ? &Z.dx[0][wr][l32] : &B.dx[0][wr][l32];
-        const uint16_t* dwp0 = half ? &Z.dw[0][ct0][l32] : &B.dw[0][ct0][l32];
-        const uint16_t* dwp1 = half ? &Z.dw[0][ct1][l32] : &B.dw[0][ct1][l32];
-        constexpr int kDxB = 2 * 32, kDwB = 4 * 32;  // element strides between blocks
-        v16i I0, I1;
-        v16f S0, S1;
-        auto issue = [&](int b) {
-          const v4i a = *reinterpret_cast<const v4i*>(arow + b * 32);
-          I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-              a, *reinterpret_cast<const v4i*>(brow0 + b * 32), izero, 0, 0, 0);
-          I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-              a, *reinterpret_cast<const v4i*>(brow1 + b * 32), izero, 0, 0, 0);
-          op_dx[0] = dxp[b * kDxB];
-          op_dw0[0] = dwp0[b * kDwB];
-          op_dw1[0] = dwp1[b * kDwB];
-          const v8h sdx = __builtin_bit_cast(v8h, op_dx);
-          S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              sdx, __builtin_bit_cast(v8h, op_dw0), fzero, 0, 0, 0);
-          S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              sdx, __builtin_bit_cast(v8h, op_dw1), fzero, 0, 0, 0);
-        };
-#pragma unroll
-        for (int b = 0; b < kKB; ++b) {
-          // (issuing the next block's MFMAs ahead of this block's VALU needs ~290 registers and
-          // halves the occupancy; two resident wavefronts per SIMD interleave instead)
-          issue(b);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
-            acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
-          }
-        }
-        if (WT == 1) {
-          // sum over the stage's 4 blocks of mw * sx: lanes 0..31 carry blocks 0,1 and lanes
-          // 32..63 blocks 2,3 of the same rows, so no k slot is wasted on zeros
-          op_dx[0] = (int)B.sx[32 * wr + l32][half];
-          op_dw0[0] = (int)B.mw[32 * ct0 + l32][half];
-          op_dw1[0] = (int)B.mw[32 * ct1 + l32][half];
-          const v8h sxo = __builtin_bit_cast(v8h, op_dx);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxo, __builtin_bit_cast(v8h, op_dw0),
-                                                        acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxo, __builtin_bit_cast(v8h, op_dw1),
-                                                        acc1, 0, 0, 0);
         }
       }
+      return;
     }
-    if (s + 1 < nstages) store_stage<WT>(L[(s + 1) & 1], st);
-    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < kKB; ++b) {
+      const v4i a = a_frag<WT>(arow, b, half);
+      const v16i I0 =
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow0, b, half), izero, 0, 0, 0);
+      const v16i I1 =
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow1, b, half), izero, 0, 0, 0);
+      // 2 * dx * dw: the q8_1 header dword of block b is (d, s); the weight's d is
+      // zero-extended, so the s half meets a zero
+      op_x[0] = (int)lds_u32(arow + 4 * b);
+      op_w0[0] = (int)b_scale<WT>(brow0, b);
+      op_w1[0] = (int)b_scale<WT>(brow1, b);
+      const v8h sx = __builtin_bit_cast(v8h, op_x);
+      const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, __builtin_bit_cast(v8h, op_w0),
+                                                             fzero, 0, 0, 0);
+      const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, __builtin_bit_cast(v8h, op_w1),
+                                                             fzero, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
+        acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
+      }
+    }
+    if (WT == 1) {
+      // 2 * sum over the stage's blocks of mw * sx: the q8_1 header (d0,s0,...,d3,s3) against
+      // (0,m0,...,0,m3), the m taken from the high half of each block's first dword
+      const v4i hdr = *reinterpret_cast<const v4i*>(arow);
+      v4i m0, m1;
+#pragma unroll
+      for (int b = 0; b < kKB; ++b) {
+        m0[b] = (int)(lds_u32(brow0 + 20 * b) & 0xffff0000u);
+        m1[b] = (int)(lds_u32(brow1 + 20 * b) & 0xffff0000u);
+      }
+      const v8h hx = __builtin_bit_cast(v8h, hdr);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(hx, __builtin_bit_cast(v8h, m0), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(hx, __builtin_bit_cast(v8h, m1), acc1, 0, 0, 0);
+    }
+  };
+
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the previous tile
+  __builtin_amdgcn_s_barrier();        // ... and every other wave's, before the ring refills
+  issue(L0, 0);
+  if (nstages > 1) issue(L1, 1);
+  for (int s0 = 0; s0 < nstages; s0 += 3) {
+    step(s0, L0, L2);
+    if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
+    if (s0 + 2 < nstages) step(s0 + 2, L2, L1);
   }
   if (EPI == 2 || !live) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // remove the factor 2 of the doubled scales (exact)
+    acc0[i] *= 0.5f;
+    acc1[i] *= 0.5f;
+  }
 
   if (EPI == 0) {
     float* out = reinterpret_cast<float*>(p.out);
@@ -331,28 +398,24 @@ __device__ __forceinline__ void mmq_tile(Buf (&L)[2], const Zeros& Z, const MmqP
 }
 
 template <int WT, int EPI>
-__global__ __launch_bounds__(256) void mmq_layer_kernel(MmqProblem p) {
-  __shared__ Buf L[2];
-  __shared__ Zeros Z;
+__global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
+  __shared__ StageBuf<WT> L0, L1, L2;
   const int mt = blockIdx.y;
   if (mt >= *p.n_tiles) return;
-  zero_shadow(Z);
   const MTile t = p.tiles[mt];
   const uint8_t* W = p.wbase + (size_t)t.ordinal * p.pos_stride + p.mat_offset;
-  mmq_tile<WT, EPI>(L, Z, p, W, t.row0, t.nrows, blockIdx.x);
+  mmq_tile<WT, EPI>(L0, L1, L2, p, W, t.row0, t.nrows, blockIdx.x);
 }
 
 template <int WT, int EPI>
-__global__ __launch_bounds__(256) void mmq_group_kernel(MmqProblem p) {
-  __shared__ Buf L[2];
-  __shared__ Zeros Z;
-  zero_shadow(Z);
+__global__ __launch_bounds__(256, 2) void mmq_group_kernel(MmqProblem p) {
+  __shared__ StageBuf<WT> L0, L1, L2;
   const int j = blockIdx.z;
   const int e = p.experts[j];
   const int r0 = p.offsets[e], cnt = p.offsets[e + 1] - r0;
   const uint8_t* W = p.wbase + (size_t)j * p.pos_stride + p.mat_offset;
   for (int m = blockIdx.y; m * kRowsM < cnt; m += gridDim.y)
-    mmq_tile<WT, EPI>(L, Z, p, W, r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM),
+    mmq_tile<WT, EPI>(L0, L1, L2, p, W, r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM),
                       blockIdx.x);
 }
 
