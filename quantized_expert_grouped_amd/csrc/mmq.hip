@@ -74,20 +74,8 @@ __device__ __forceinline__ int weight_row(int epi, int nb, int n0, int n_out) {
   return epi == 1 ? (nb < 64 ? n0 + nb : n_out + n0 + nb - 64) : n0 + nb;
 }
 
-// s_waitcnt vmcnt(n) with the other counters left alone (n is wave-uniform, at most 20 here)
-__device__ __forceinline__ void wait_vm(int n) {
-#define MOE_VM(k) \
-  case k:         \
-    __builtin_amdgcn_s_waitcnt(((k)&0xF) | (((k) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); \
-    break;
-  switch (n) {
-    MOE_VM(0) MOE_VM(1) MOE_VM(2) MOE_VM(3) MOE_VM(4) MOE_VM(5) MOE_VM(6) MOE_VM(7) MOE_VM(8)
-    MOE_VM(9) MOE_VM(10) MOE_VM(11) MOE_VM(12) MOE_VM(13) MOE_VM(14) MOE_VM(15) MOE_VM(16)
-    MOE_VM(17) MOE_VM(18) MOE_VM(19) MOE_VM(20)
-    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;  // vmcnt(0)
-  }
-#undef MOE_VM
-}
+// s_waitcnt immediate for vmcnt(n) (0 <= n < 64) with the other counters left alone
+constexpr int vm_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Each lane's byte offsets of its DMA pieces, relative to the stage's first byte in global
 // memory; fixed for a tile, the stage advance is added to the (uniform) base pointer.
@@ -126,13 +114,12 @@ __device__ __forceinline__ void plan_dma(DmaPlan<WT>& d, size_t act_row_bytes, i
   }
 }
 
+// DMA instructions issued per stage by the wavefront that issues the fewest (wavefront w issues
+// instructions w, w+4, ... of each operand).  Waiting until at most this many loads are in
+// flight completes the current stage on every wavefront; a wavefront that issues more also waits
+// for its first extra loads of the next stage, which only shortens its lookahead.
 template <int WT>
-__device__ __forceinline__ int dma_count() {  // DMA instructions this wavefront issues per stage
-  const int wave = wave_id();
-  const int na = (kAInstr - wave + 3) / 4;
-  const int nb = (Geo<WT>::kBInstr - wave + 3) / 4;
-  return na + nb;
-}
+constexpr int kMinDmaPerStage = kAInstr / 4 + Geo<WT>::kBInstr / 4;
 
 // One direct global->LDS load: lane i's 16 (or 4) bytes land at lds + 16*i (4*i), lds
 // wave-uniform (it is passed in M0).  Written as inline assembly so that the compiler's wait-count
@@ -239,7 +226,6 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
 
   DmaPlan<WT> plan;
   plan_dma<WT>(plan, act_row_bytes, nrows, row_bytes, EPI, n0, p.n_out);
-  const int per_stage = dma_count<WT>();
 
   v16f acc0, acc1;
 #pragma unroll
@@ -262,8 +248,11 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   // can tell the reads of one from the loads into another and keeps the loads in flight.
   auto step = [&](int s, const StageBuf<WT>& cur, StageBuf<WT>& fill) {
     // (the raw block-dot epilogue also stores inside the loop, so it drains the counter)
-    const int ahead = EPI == 2 ? 0 : min(1, nstages - 1 - s);
-    wait_vm(ahead * per_stage);
+    const bool ahead = EPI != 2 && s + 1 < nstages;
+    if (ahead)
+      __builtin_amdgcn_s_waitcnt(vm_imm(kMinDmaPerStage<WT>));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_imm(0));
     __builtin_amdgcn_s_barrier();
     if (s + 2 < nstages) issue(fill, s + 2);
     if (!live) return;
@@ -397,14 +386,29 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   }
 }
 
+// The dispatcher hands workgroups to the 8 XCDs round-robin in launch order, and each XCD has
+// its own L2.  The live (m-tile, n-tile) pairs are therefore renumbered so that XCD x receives
+// one contiguous run of them, m-tile major: the n-tiles of an m-tile share its activation rows
+// in one L2, and consecutive m-tiles of an expert share its weights there.
+constexpr int kXcds = 8;
+
 template <int WT, int EPI>
 __global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
   __shared__ StageBuf<WT> L0, L1, L2;
-  const int mt = blockIdx.y;
-  if (mt >= *p.n_tiles) return;
+  const int ntl = gridDim.x;
+  const int live = ntl * *p.n_tiles;
+  const int id = blockIdx.x + ntl * blockIdx.y;
+  if (id >= live) return;
+#ifdef MOE_MMQ_NO_XCD_ORDER
+  const int work = id;
+#else
+  const int xcd = id % kXcds;
+  const int work = xcd * (live / kXcds) + min(xcd, live % kXcds) + id / kXcds;
+#endif
+  const int mt = work / ntl;
   const MTile t = p.tiles[mt];
   const uint8_t* W = p.wbase + (size_t)t.ordinal * p.pos_stride + p.mat_offset;
-  mmq_tile<WT, EPI>(L0, L1, L2, p, W, t.row0, t.nrows, blockIdx.x);
+  mmq_tile<WT, EPI>(L0, L1, L2, p, W, t.row0, t.nrows, work % ntl);
 }
 
 template <int WT, int EPI>
