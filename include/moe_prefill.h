@@ -29,6 +29,15 @@
  *                             qs[j]: element j in the low nibble, element j+16 in the high nibble
  *   expert, expert_bytes    : gate [F rows x H/32 blocks] | up [F x H/32] | down [H x F/32],
  *                             each matrix row-major with its blocks along the reduction dimension
+ *   MMQ layout of an expert : what moe_gather_group_mmq writes and moe_mmq_grouped reads (this
+ *                             library's choice; the pages only require the gathered experts to
+ *                             feed the matmul).  Same order gate | up | down and the same size;
+ *                             each matrix of n_rows rows and nblk blocks per row is stored as tiles
+ *                             of 64 rows by 4 blocks: for tile j, stage t, row i < 64 (row 64j+i),
+ *                             the row's blocks 4t..4t+3 take G = 4 * block bytes at byte
+ *                             ((j * nblk/4 + t) * 64 + i) * G, headers first:
+ *                               Q4_1 (G = 80) : (d, m) of the 4 blocks, then their qs[16]
+ *                               Q8_0 (G = 136): d of the 4 blocks, then their q[32]
  *   q8_1 row of n values    : n/128 groups of 144 B: (fp16 d, fp16 s) of its 4 blocks of 32, then
  *                             the 4 blocks' int8 q.  d = amax/127 (fp32), q = roundf(v/d), s = d*sum q
  *                             ([QS] opening section and "Identity": the DS4 layout, which carries the
@@ -44,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_GROUP 16     /* experts per group buffer ([G1] "What": MMQ_GROUP = 16) */
 #define MOE_MAX_E 2048       /* largest expert count the kernels accept */
 #define MOE_MAX_K 64         /* largest routes per token */
@@ -109,13 +118,23 @@ int moe_quantize_scatter_q8_1(const float *x, int T, int H, int K, const int32_t
 int moe_gather_group(const void *const *src_ptrs, int n, size_t expert_bytes, void *group_buf,
                      int first_pos, size_t pos_stride, void *stream);
 
+/* a3  The same gather writing each expert in the MMQ layout, the form moe_mmq_grouped reads and
+ * the layer uses.  src_ptrs [host]: n (1..16) device pointers to raw experts of
+ * moe_expert_bytes(H, F, wtype) bytes; positions as in moe_gather_group, pos_stride >= that size
+ * when n > 1.  H and F: multiples of 128.  Experts at 16-byte (Q4_1) or 8-byte (Q8_0) aligned
+ * addresses, with a group_buf position of the same alignment, move in whole words; others take a
+ * byte-wise path with the same result. */
+int moe_gather_group_mmq(const void *const *src_ptrs, int n, int wtype, int H, int F,
+                         void *group_buf, int first_pos, size_t pos_stride, void *stream);
+
 /* a4..a6  Grouped quantised matmul (MMQ) over one group buffer ([G2] "What changes", [QS] opening
- * section).  Position j < n_group of group_buf (at j*pos_stride) holds expert group_experts[j]
+ * section).  Position j < n_group of group_buf (at j*pos_stride) holds expert group_experts[j] in the
+ * MMQ layout (moe_gather_group_mmq)
  * ([host] array, each in [0, E)); its rows are offsets[e] .. offsets[e+1]-1 (offsets: int32 [E+1],
  * device) of act_q8 (q8_1 rows of k_in values,
  * grouped by expert as moe_build_maps orders them).  The weight matrix starts mat_offset bytes into
- * each expert and has n_out rows of k_in/32 blocks (for MOE_EPI_SWIGLU_Q8_1: gate = rows 0..n_out-1,
- * up = rows n_out..2*n_out-1).  Per block b: I_b = integer dot of the 32 int8 (Q8_0) or 4-bit (Q4_1)
+ * each expert and has n_out rows of k_in/32 blocks (for MOE_EPI_SWIGLU_Q8_1 that matrix is gate and
+ * up is the next matrix, n_out*k_in/32 blocks further).  Per block b: I_b = integer dot of the 32 int8 (Q8_0) or 4-bit (Q4_1)
  * weights with the 32 int8 activations; y_b = dw*dx*I_b (+ mw*sx for Q4_1); a row's result is the
  * sum over b.  Output row r is written at row r of `out` (rows of other experts untouched):
  *   MOE_EPI_F32:           fp32 [* x n_out]

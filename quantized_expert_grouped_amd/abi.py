@@ -39,6 +39,7 @@ SIGNATURES = {
     "moe_build_maps": (I, [P, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
     "moe_quantize_scatter_q8_1": (I, [P, I, I, I, P, P, I, P, P]),
     "moe_gather_group": (I, [P, I, SZ, P, I, SZ, P]),
+    "moe_gather_group_mmq": (I, [P, I, I, I, I, P, I, SZ, P]),
     "moe_mmq_grouped": (I, [I, P, SZ, SZ, I, I, P, I, P, I, P, I, P, P, P]),
     "moe_combine": (I, [P, P, P, I, I, I, P, P]),
     "moe_prefill_layer": (I, [P, I, I, I, I, I, P, P, I, P, P, SZ, I, I, P, SZ, P, P]),
@@ -159,6 +160,19 @@ def raw_gather_group(src_ptrs, expert_bytes_, group_buf, first_pos, pos_stride, 
 def gather_group(src_ptrs, expert_bytes_, group_buf, first_pos, pos_stride, stream=None):
     _check("moe_gather_group", raw_gather_group(src_ptrs, expert_bytes_, group_buf, first_pos,
                                                 pos_stride, stream))
+
+
+def raw_gather_group_mmq(src_ptrs, wtype, H, F, group_buf, first_pos, pos_stride, stream=None):
+    n = len(src_ptrs)
+    arr = (ctypes.c_void_p * max(n, 1))(*[int(p) for p in src_ptrs])
+    return lib().moe_gather_group_mmq(ctypes.cast(arr, ctypes.c_void_p) if n else None, n, wtype,
+                                      H, F, _ptr(group_buf), first_pos, pos_stride,
+                                      _stream(stream))
+
+
+def gather_group_mmq(src_ptrs, wtype, H, F, group_buf, first_pos, pos_stride, stream=None):
+    _check("moe_gather_group_mmq", raw_gather_group_mmq(src_ptrs, wtype, H, F, group_buf,
+                                                        first_pos, pos_stride, stream))
 
 
 def raw_mmq_grouped(wtype, group_buf, pos_stride, mat_offset, n_out, k_in, group_experts,

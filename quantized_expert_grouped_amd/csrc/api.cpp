@@ -177,6 +177,23 @@ int moe_gather_group(const void* const* src_ptrs, int n, size_t expert_bytes, vo
                                        first_pos, pos_stride, as_stream(stream)));
 }
 
+int moe_gather_group_mmq(const void* const* src_ptrs, int n, int wtype, int H, int F,
+                         void* group_buf, int first_pos, size_t pos_stride, void* stream) {
+  if (!src_ptrs || !group_buf || n < 1 || n > MOE_MAX_GROUP || first_pos < 0 ||
+      first_pos + n > MOE_MAX_GROUP)
+    return MOE_EINVAL;
+  if (!valid_wtype(wtype)) return MOE_EUNSUPPORTED;
+  if (H < 128 || H % 128 != 0 || F < 128 || F % 128 != 0) return MOE_EUNSUPPORTED;
+  if (n > 1 && pos_stride < moe_expert_bytes(H, F, wtype)) return MOE_EINVAL;
+  GatherPtrs p{};
+  for (int j = 0; j < n; ++j) {
+    if (!src_ptrs[j]) return MOE_EINVAL;
+    p.src[j] = static_cast<const uint8_t*>(src_ptrs[j]);
+  }
+  return status_of(launch_gather_group_mmq(p, n, wtype, H, F, static_cast<uint8_t*>(group_buf),
+                                           first_pos, pos_stride, as_stream(stream)));
+}
+
 int moe_mmq_grouped(int wtype, const void* group_buf, size_t pos_stride, size_t mat_offset,
                     int n_out, int k_in, const int32_t* group_experts, int n_group,
                     const int32_t* offsets, int E, const void* act_q8, int epilogue, void* out,
@@ -258,9 +275,9 @@ int moe_prefill_layer(const float* x, int T, int H, int F, int E, int K, const i
   if ((e = launch_quantize(x, T, H, K, mo.slot, mo.src, 0, base + L.q8x, s)) != hipSuccess)
     return MOE_EHIP;
   mark(2);
-  if ((e = launch_gather_all(static_cast<const uint8_t*>(pool), expert_off, mo.order, mo.n_active,
-                             E, group_size, expert_bytes, base + L.groups, L.group_stride, s)) !=
-      hipSuccess)
+  if ((e = launch_gather_all_mmq(static_cast<const uint8_t*>(pool), expert_off, mo.order,
+                                 mo.n_active, E, group_size, wtype, H, F, base + L.groups,
+                                 L.group_stride, s)) != hipSuccess)
     return MOE_EHIP;
   mark(3);
   MmqProblem gu{};

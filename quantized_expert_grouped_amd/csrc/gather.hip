@@ -20,6 +20,7 @@ namespace moe {
 namespace {
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 4;
@@ -71,6 +72,145 @@ __global__ __launch_bounds__(kGatherThreads) void gather_all_kernel(
             gridDim.x);
 }
 
+// ---- the MMQ layout -------------------------------------------------------------------------
+// The grouped matmul stages its weights as tiles of 64 rows by 128 values (4 blocks), so the
+// group buffer holds every matrix as those tile-stages, each one contiguous: for tile j, stage
+// t and row i < 64 (matrix row 64j+i), the row's blocks 4t..4t+3 sit at byte
+// ((j * stages + t) * 64 + i) * G, G = 4 * block bytes, with the blocks' headers first:
+//   Q4_1, G = 80 : (d, m) of the 4 blocks, then their qs[16]
+//   Q8_0, G = 136: d of the 4 blocks, then their q[32]
+// The expert keeps its order (gate | up | down) and its size.  A 64-row tile is one contiguous
+// run in the raw expert and one in the packed expert, so a workgroup moves a tile's rows for
+// up to kPackStages stages: it reads the rows' bytes into LDS with wide coalesced loads and
+// writes the tile-stages out, also coalesced, picking each output word from LDS.
+
+constexpr int kPackStages = 4;
+
+template <int WT>
+struct Pack {
+  static constexpr int kG = WT == 1 ? 80 : 136;
+  static constexpr int kLds = 64 * kPackStages * kG;
+};
+
+// Byte offset, within a row's 4-block group in the raw layout, of the low half of output word k
+// of the packed group (the high half is 2 bytes further).  Every such offset is even.
+template <int WT>
+__device__ __forceinline__ int packed_word_src(int k) {
+  if (WT == 1) return k < 4 ? 20 * k : 20 * ((k - 4) >> 2) + 4 + 4 * ((k - 4) & 3);
+  if (k < 2) return 68 * k;  // (d_{2k}, d_{2k+1}) live at 68k and 68k + 34
+  return 34 * ((k - 2) >> 3) + 2 + 4 * ((k - 2) & 7);
+}
+
+template <int WT>
+__device__ __forceinline__ uint32_t packed_word(const uint8_t* grp, int k) {
+  const int o = packed_word_src<WT>(k);
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(grp);
+  if (WT == 1) return *reinterpret_cast<const uint32_t*>(grp + o);  // 4-byte aligned
+  const uint32_t lo = h[o >> 1];
+  const uint32_t hi = h[(k < 2 ? o + 34 : o + 2) >> 1];
+  return lo | (hi << 16);
+}
+
+// One work item: tile `tile` of matrix `mat` (0 gate, 1 up, 2 down), stages t0 .. t0+ns-1.
+template <int WT>
+__device__ __forceinline__ void pack_item(const uint8_t* __restrict__ src_e,
+                                          uint8_t* __restrict__ dst_e, int H, int F, int item,
+                                          uint8_t* lds) {
+  constexpr int G = Pack<WT>::kG;
+  const int sh = H / 128, sf = F / 128;
+  const int cg = (sh + kPackStages - 1) / kPackStages, cd = (sf + kPackStages - 1) / kPackStages;
+  const int items_gu = (F / 64) * cg;
+  int tile, chunk, nS;
+  size_t mat_off;
+  if (item < 2 * items_gu) {
+    const int mat = item / items_gu, r = item % items_gu;
+    tile = r / cg, chunk = r % cg, nS = sh;
+    mat_off = (size_t)mat * F * sh * G;
+  } else {
+    const int r = item - 2 * items_gu;
+    tile = r / cd, chunk = r % cd, nS = sf;
+    mat_off = (size_t)2 * F * sh * G;
+  }
+  const size_t row_bytes = (size_t)nS * G;
+  const int t0 = chunk * kPackStages, ns = min(kPackStages, nS - t0);
+  const int seg = ns * G;  // bytes of one row in this item
+  const uint8_t* s = src_e + mat_off + (size_t)tile * 64 * row_bytes + (size_t)t0 * G;
+  uint8_t* d = dst_e + mat_off + ((size_t)tile * nS + t0) * 64 * G;
+  const int tid = threadIdx.x;
+
+  // rows -> LDS (row i at i * seg), in the widest pieces the alignment allows
+  if (((uintptr_t)s & 15) == 0 && (row_bytes & 15) == 0 && (seg & 15) == 0) {
+    const int per_row = seg / 16, total = 64 * per_row;
+    for (int q = tid; q < total; q += kGatherThreads) {
+      const int i = q / per_row, k = q % per_row;
+      *reinterpret_cast<v4u*>(lds + 16 * q) =
+          __builtin_nontemporal_load(reinterpret_cast<const v4u*>(s + i * row_bytes + 16 * k));
+    }
+  } else if (((uintptr_t)s & 7) == 0 && (row_bytes & 7) == 0) {
+    const int per_row = seg / 8, total = 64 * per_row;
+    for (int q = tid; q < total; q += kGatherThreads) {
+      const int i = q / per_row, k = q % per_row;
+      *reinterpret_cast<v2u*>(lds + 8 * q) =
+          __builtin_nontemporal_load(reinterpret_cast<const v2u*>(s + i * row_bytes + 8 * k));
+    }
+  } else {
+    for (int q = tid; q < 64 * seg; q += kGatherThreads) {
+      const int i = q / seg, k = q % seg;
+      lds[q] = s[i * row_bytes + k];
+    }
+  }
+  __syncthreads();
+
+  // LDS -> the ns tile-stages (one contiguous run of ns * 64 * G bytes), 16 bytes per lane
+  constexpr int words = G / 4;  // per packed group
+  const int total16 = ns * 64 * G / 16;
+  const bool wide = ((uintptr_t)d & 15) == 0;
+  for (int q = tid; q < total16; q += kGatherThreads) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int w = 4 * q + u;                    // word of the run
+      const int st = w / (64 * words), ww = w % (64 * words);
+      const int i = ww / words, k = ww % words;   // row of the tile, word of its group
+      v[u] = packed_word<WT>(lds + i * seg + st * G, k);
+    }
+    if (wide) {
+      reinterpret_cast<v4u*>(d)[q] = (v4u){v[0], v[1], v[2], v[3]};
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) d[16 * q + 4 * u + b] = (uint8_t)(v[u] >> (8 * b));
+    }
+  }
+  __syncthreads();  // the LDS is reused by the next item of this workgroup
+}
+
+int pack_items(int H, int F) {
+  const int sh = H / 128, sf = F / 128;
+  return 2 * (F / 64) * ((sh + kPackStages - 1) / kPackStages) +
+         (H / 64) * ((sf + kPackStages - 1) / kPackStages);
+}
+
+template <int WT>
+__global__ __launch_bounds__(kGatherThreads) void gather_mmq_group_kernel(
+    GatherPtrs p, int H, int F, uint8_t* __restrict__ dst, int first_pos, size_t pos_stride) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Pack<WT>::kLds];
+  const int j = blockIdx.y;
+  pack_item<WT>(p.src[j], dst + (size_t)(first_pos + j) * pos_stride, H, F, blockIdx.x, lds);
+}
+
+template <int WT>
+__global__ __launch_bounds__(kGatherThreads) void gather_mmq_all_kernel(
+    const uint8_t* __restrict__ pool, const int64_t* __restrict__ expert_off,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ n_active, int H, int F,
+    uint8_t* __restrict__ dst, size_t stride) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Pack<WT>::kLds];
+  const int pos = blockIdx.z * gridDim.y + blockIdx.y;
+  if (pos >= *n_active) return;
+  pack_item<WT>(pool + expert_off[order[pos]], dst + (size_t)pos * stride, H, F, blockIdx.x, lds);
+}
+
 int parts_for(size_t bytes) {
   // about 4 grid-stride trips of 16 KiB per workgroup
   const size_t per = (size_t)kGatherThreads * kGatherUnroll * 16 * 4;
@@ -97,6 +237,32 @@ hipError_t launch_gather_all(const uint8_t* pool, const int64_t* expert_off, con
   const dim3 grid(parts_for(bytes), group_size, groups);
   gather_all_kernel<<<grid, kGatherThreads, 0, s>>>(pool, expert_off, order, n_active, bytes,
                                                     dst, stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_group_mmq(const GatherPtrs& p, int n, int wtype, int H, int F,
+                                   uint8_t* dst, int first_pos, size_t pos_stride,
+                                   hipStream_t s) {
+  const dim3 grid(pack_items(H, F), n);
+  if (wtype == 1)
+    gather_mmq_group_kernel<1><<<grid, kGatherThreads, 0, s>>>(p, H, F, dst, first_pos, pos_stride);
+  else
+    gather_mmq_group_kernel<0><<<grid, kGatherThreads, 0, s>>>(p, H, F, dst, first_pos, pos_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_all_mmq(const uint8_t* pool, const int64_t* expert_off,
+                                 const int32_t* order, const int32_t* n_active, int max_slots,
+                                 int group_size, int wtype, int H, int F, uint8_t* dst,
+                                 size_t stride, hipStream_t s) {
+  const int groups = (max_slots + group_size - 1) / group_size;
+  const dim3 grid(pack_items(H, F), group_size, groups);
+  if (wtype == 1)
+    gather_mmq_all_kernel<1><<<grid, kGatherThreads, 0, s>>>(pool, expert_off, order, n_active, H,
+                                                             F, dst, stride);
+  else
+    gather_mmq_all_kernel<0><<<grid, kGatherThreads, 0, s>>>(pool, expert_off, order, n_active, H,
+                                                             F, dst, stride);
   return hipGetLastError();
 }
 

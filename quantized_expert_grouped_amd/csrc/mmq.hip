@@ -27,11 +27,13 @@
 //     hold one block of 32 features;
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
 // K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of LDS
-// buffers with direct global->LDS loads (global_load_lds_dwordx4; 4-byte pieces for Q8_0, whose
-// 34-byte blocks leave rows only 8-byte aligned), two stages ahead of the MFMAs (a ring of three), so the
-// registers hold no staged data and no VALU moves it.  Fragments are read from the raw bytes:
-// q8_1 rows keep their 144-byte groups, Q8_0 blocks are realigned with v_alignbit, Q4_1 nibbles
-// are split with two masks: a lane half h takes elements 8h..8h+7 and 16+8h..16+8h+7 of a block
+// buffers with direct global->LDS loads (global_load_lds_dwordx4), two stages ahead of the MFMAs
+// (a ring of three), so the registers hold no staged data and no VALU moves it.  The weights come
+// from the group buffer's MMQ layout (64-row tiles of one stage, each contiguous, every row's
+// block headers first), so a workgroup's weight stage is two contiguous runs, and in LDS the
+// rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart, a stride at which the 8- and 16-byte fragment
+// reads of 32 rows hit distinct banks.  q8_1 rows keep their 144-byte groups.  Q4_1 nibbles are
+// split with two masks: a lane half h takes elements 8h..8h+7 and 16+8h..16+8h+7 of a block
 // (8 packed bytes), on both operands, so the int8 dot product is unchanged.
 #include <math.h>
 
@@ -55,12 +57,16 @@ constexpr int kKB = 4;            // blocks per stage
 constexpr int kARow = 144;        // bytes of one q8_1 group (the stage's slice of a row)
 constexpr int kAInstr = kRowsM * kARow / (64 * 16);  // 9 DMA instructions per stage
 
+// Weights arrive in the MMQ layout the gather writes: each matrix as tiles of 64 rows by one
+// stage (4 blocks), every tile-stage contiguous, a row's 4 blocks headers first (Q4_1: 4 x (d, m)
+// then 4 x qs[16], 80 B; Q8_0: 4 x d then 4 x q[32], 136 B).  A workgroup's stage is two such
+// tile-stages, copied verbatim into LDS rows 0..63 and 64..127.
 template <int WT>
 struct Geo {
-  static constexpr int kBRow = WT == 0 ? 4 * 34 : 4 * 20;  // raw bytes of a row per stage
-  static constexpr int kBChunk = WT == 0 ? 4 : 16;         // bytes per lane per DMA
-  static constexpr int kBInstr = kRowsN * kBRow / (64 * kBChunk);  // 68 or 10
-  static constexpr int kBPerWave = (kBInstr + 3) / 4;              // 17 or 3
+  static constexpr int kBRow = WT == 0 ? 4 * 34 : 4 * 20;          // bytes of a row per stage
+  static constexpr int kTilePieces = 64 * kBRow / 16;              // 16-byte pieces per tile-stage
+  static constexpr int kBInstr = 2 * kTilePieces / 64;             // 17 or 10
+  static constexpr int kBPerWave = (kBInstr + 3) / 4;              // 5 or 3
 };
 
 template <int WT>
@@ -68,11 +74,6 @@ struct alignas(16) StageBuf {
   uint8_t a[kRowsM * kARow];
   uint8_t b[kRowsN * Geo<WT>::kBRow];
 };
-
-__device__ __forceinline__ int weight_row(int epi, int nb, int n0, int n_out) {
-  // SwiGLU tiles hold gate features n0.. in LDS rows 0..63 and the same up features in 64..127
-  return epi == 1 ? (nb < 64 ? n0 + nb : n_out + n0 + nb - 64) : n0 + nb;
-}
 
 // s_waitcnt immediate for vmcnt(n) (0 <= n < 64) with the other counters left alone
 constexpr int vm_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -89,9 +90,11 @@ __device__ __forceinline__ int wave_id() {  // uniform across the wavefront, kep
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// tile0 / tile1: byte offsets (from the weight pointer) of the two 64-row tiles whose stage 0
+// fills LDS rows 0..63 and 64..127; stage t adds t * 64 * kBRow to both.
 template <int WT>
 __device__ __forceinline__ void plan_dma(DmaPlan<WT>& d, size_t act_row_bytes, int nrows,
-                                         size_t row_bytes, int epi, int n0, int n_out) {
+                                         size_t tile0, size_t tile1) {
   const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
@@ -101,16 +104,9 @@ __device__ __forceinline__ void plan_dma(DmaPlan<WT>& d, size_t act_row_bytes, i
   }
 #pragma unroll
   for (int j = 0; j < Geo<WT>::kBPerWave; ++j) {
-    const int c = 64 * (wave + 4 * j) + lane;
-    if (WT == 0) {
-      const int row = c / 34;  // 34 dwords of a row's 4 blocks
-      d.b[j] = (uint32_t)(weight_row(epi, min(row, kRowsN - 1), n0, n_out) * row_bytes +
-                          (c % 34) * 4);
-    } else {
-      const int row = c / 5;  // 5 pieces of a row's 4 blocks
-      d.b[j] = (uint32_t)(weight_row(epi, min(row, kRowsN - 1), n0, n_out) * row_bytes +
-                          (c % 5) * 16);
-    }
+    const int c = min(64 * (wave + 4 * j) + lane, 2 * Geo<WT>::kTilePieces - 1);
+    const int k = Geo<WT>::kTilePieces;
+    d.b[j] = (uint32_t)(c < k ? tile0 + 16 * c : tile1 + 16 * (c - k));
   }
 }
 
@@ -137,10 +133,6 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "{m0}"(lds), "v"(g) : "memory");
 }
 
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %1, off" : : "{m0}"(lds), "v"(g) : "memory");
-}
-
 template <int WT>
 __device__ __forceinline__ void issue_stage(StageBuf<WT>& S, const DmaPlan<WT>& d,
                                             const uint8_t* abase, const uint8_t* wbase) {
@@ -153,17 +145,8 @@ __device__ __forceinline__ void issue_stage(StageBuf<WT>& S, const DmaPlan<WT>& 
 #pragma unroll
   for (int j = 0; j < Geo<WT>::kBPerWave; ++j) {
     const int i = wave + 4 * j;
-    if (i < Geo<WT>::kBInstr) {
-      if (WT == 0)
-        dma4(wbase + d.b[j], lds_address(S.b + i * 64 * 4));
-      else
-        dma16(wbase + d.b[j], lds_address(S.b + i * 64 * 16));
-    }
+    if (i < Geo<WT>::kBInstr) dma16(wbase + d.b[j], lds_address(S.b + i * 64 * 16));
   }
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
 }
 
 // int8 MFMA operands of block b.  Q4_1: lane half h takes elements 8h..8h+7, 16+8h..16+8h+7.
@@ -179,31 +162,28 @@ __device__ __forceinline__ v4i a_frag(const uint8_t* arow, int b, int half) {
   return *reinterpret_cast<const v4i*>(q + 16 * half);
 }
 
+// Weight operand of block b from a row's stage bytes (headers first).  Rows are 80 or 136 bytes
+// apart, so 8- and 16-byte reads of 32 consecutive rows hit distinct LDS banks.
 template <int WT>
 __device__ __forceinline__ v4i b_frag(const uint8_t* brow, int b, int half) {
   if (WT == 1) {
-    const uint8_t* q = brow + 20 * b + 4 + 8 * half;  // 4-byte aligned
-    const uint32_t x0 = lds_u32(q), x1 = lds_u32(q + 4);
+    const uint2 x = *reinterpret_cast<const uint2*>(brow + 16 + 16 * b + 8 * half);
     const uint32_t m = 0x0f0f0f0fu;
-    return (v4i){(int)(x0 & m), (int)(x1 & m), (int)((x0 >> 4) & m), (int)((x1 >> 4) & m)};
+    return (v4i){(int)(x.x & m), (int)(x.y & m), (int)((x.x >> 4) & m), (int)((x.y >> 4) & m)};
   }
-  if ((b & 1) == 0) {  // q of an even block starts 2 bytes past a 4-byte boundary
-    const uint8_t* p = brow + 34 * b + 16 * half;
-    uint32_t w[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) w[i] = lds_u32(p + 4 * i);
-    return (v4i){(int)__builtin_amdgcn_alignbit(w[1], w[0], 16),
-                 (int)__builtin_amdgcn_alignbit(w[2], w[1], 16),
-                 (int)__builtin_amdgcn_alignbit(w[3], w[2], 16),
-                 (int)__builtin_amdgcn_alignbit(w[4], w[3], 16)};
-  }
-  const uint8_t* p = brow + 34 * b + 2 + 16 * half;
-  return (v4i){(int)lds_u32(p), (int)lds_u32(p + 4), (int)lds_u32(p + 8), (int)lds_u32(p + 12)};
+  const uint8_t* q = brow + 8 + 32 * b + 16 * half;  // 8-byte aligned
+  const uint2 lo = *reinterpret_cast<const uint2*>(q);
+  const uint2 hi = *reinterpret_cast<const uint2*>(q + 8);
+  return (v4i){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
 }
 
+// The f16 MFMA operand of a row's weight headers: Q4_1 (d_b, m_b) in fp16 slots 2b, 2b+1;
+// Q8_0 d_b in slot b (slots 4..7 zero).
 template <int WT>
-__device__ __forceinline__ uint32_t b_scale(const uint8_t* brow, int b) {  // fp16 d, zero-extended
-  return *reinterpret_cast<const uint16_t*>(brow + (WT == 1 ? 20 : 34) * b);
+__device__ __forceinline__ v4i b_header(const uint8_t* brow) {
+  if (WT == 1) return *reinterpret_cast<const v4i*>(brow);
+  const uint2 d = *reinterpret_cast<const uint2*>(brow);
+  return (v4i){(int)d.x, (int)d.y, 0, 0};
 }
 
 template <int WT, int EPI>
@@ -214,8 +194,8 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   const int wr = wave >> 1, wc = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
   const int nblk = p.k_in / kQK;
-  const size_t row_bytes = (size_t)nblk * block_bytes(WT);
   const size_t act_row_bytes = (size_t)(p.k_in / kDs4Vals) * kDs4Bytes;
+  const size_t tile_bytes = (size_t)(nblk / kKB) * 64 * Geo<WT>::kBRow;  // one 64-row tile
   const int n0 = EPI == 1 ? ntile * 64 : ntile * kRowsN;
   // the wavefront's two column tiles (32 LDS weight rows each)
   const int ct0 = EPI == 1 ? wc : 2 * wc;
@@ -224,8 +204,12 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   const int nstages = p.k_in / kDs4Vals;
   const uint8_t* abase = p.act + (size_t)row0 * act_row_bytes;
 
+  // SwiGLU: gate tile ntile and the up matrix's tile ntile; otherwise tiles 2*ntile, 2*ntile+1
+  const size_t up_offset = (size_t)p.n_out * nblk * block_bytes(WT);
+  const size_t tile0 = EPI == 1 ? ntile * tile_bytes : 2 * ntile * tile_bytes;
+  const size_t tile1 = EPI == 1 ? up_offset + ntile * tile_bytes : tile0 + tile_bytes;
   DmaPlan<WT> plan;
-  plan_dma<WT>(plan, act_row_bytes, nrows, row_bytes, EPI, n0, p.n_out);
+  plan_dma<WT>(plan, act_row_bytes, nrows, tile0, tile1);
 
   v16f acc0, acc1;
 #pragma unroll
@@ -235,11 +219,13 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   }
   const v16i izero = {0};
   const v16f fzero = {0.0f};
-  // f16 operands: dword 0 carries the fp16 value(s), the other dwords stay zero
-  v4i op_x = {0, 0, 0, 0}, op_w0 = {0, 0, 0, 0}, op_w1 = {0, 0, 0, 0};
+  // f16 operand of dx_b for block b: fp16 slot 2b (Q4_1) or b (Q8_0), every other slot zero
+  v4i za[kKB];
+#pragma unroll
+  for (int b = 0; b < kKB; ++b) za[b] = (v4i){0, 0, 0, 0};
 
   auto issue = [&](StageBuf<WT>& buf, int t) {
-    issue_stage<WT>(buf, plan, abase + (size_t)t * kARow, W + (size_t)t * Geo<WT>::kBRow);
+    issue_stage<WT>(buf, plan, abase + (size_t)t * kARow, W + (size_t)t * 64 * Geo<WT>::kBRow);
   };
 
   // One stage: wait until stage s is in LDS for every wave (which also means every wave is done
@@ -281,6 +267,10 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
       }
       return;
     }
+    // activation headers (d_b, s_b) of the row, weight headers of the two column tiles
+    const v4i hx = *reinterpret_cast<const v4i*>(arow);
+    const v8h hw0 = __builtin_bit_cast(v8h, b_header<WT>(brow0));
+    const v8h hw1 = __builtin_bit_cast(v8h, b_header<WT>(brow1));
 #pragma unroll
     for (int b = 0; b < kKB; ++b) {
       const v4i a = a_frag<WT>(arow, b, half);
@@ -288,16 +278,14 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
           __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow0, b, half), izero, 0, 0, 0);
       const v16i I1 =
           __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow1, b, half), izero, 0, 0, 0);
-      // 2 * dx * dw: the q8_1 header dword of block b is (d, s); the weight's d is
-      // zero-extended, so the s half meets a zero
-      op_x[0] = (int)lds_u32(arow + 4 * b);
-      op_w0[0] = (int)b_scale<WT>(brow0, b);
-      op_w1[0] = (int)b_scale<WT>(brow1, b);
-      const v8h sx = __builtin_bit_cast(v8h, op_x);
-      const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, __builtin_bit_cast(v8h, op_w0),
-                                                             fzero, 0, 0, 0);
-      const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, __builtin_bit_cast(v8h, op_w1),
-                                                             fzero, 0, 0, 0);
+      // 2 * dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero)
+      if (WT == 1)
+        za[b][b] = (int)((uint32_t)hx[b] & 0xffffu);
+      else
+        za[b][b >> 1] = (b & 1) ? (int)((uint32_t)hx[b] << 16) : (int)((uint32_t)hx[b] & 0xffffu);
+      const v8h sx = __builtin_bit_cast(v8h, za[b]);
+      const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
+      const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw1, fzero, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
@@ -305,18 +293,13 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
       }
     }
     if (WT == 1) {
-      // 2 * sum over the stage's blocks of mw * sx: the q8_1 header (d0,s0,...,d3,s3) against
-      // (0,m0,...,0,m3), the m taken from the high half of each block's first dword
-      const v4i hdr = *reinterpret_cast<const v4i*>(arow);
-      v4i m0, m1;
+      // 2 * sum over the stage's blocks of sx_b * mw_b: (0, s_b) against (d_b, m_b)
+      v4i hs;
 #pragma unroll
-      for (int b = 0; b < kKB; ++b) {
-        m0[b] = (int)(lds_u32(brow0 + 20 * b) & 0xffff0000u);
-        m1[b] = (int)(lds_u32(brow1 + 20 * b) & 0xffff0000u);
-      }
-      const v8h hx = __builtin_bit_cast(v8h, hdr);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(hx, __builtin_bit_cast(v8h, m0), acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(hx, __builtin_bit_cast(v8h, m1), acc1, 0, 0, 0);
+      for (int b = 0; b < kKB; ++b) hs[b] = (int)((uint32_t)hx[b] & 0xffff0000u);
+      const v8h sxs = __builtin_bit_cast(v8h, hs);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxs, hw0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxs, hw1, acc1, 0, 0, 0);
     }
   };
 

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert abi.abi_version() == 1
+    assert abi.abi_version() == 2
     assert abi.block_bytes(abi.Q8_0) == 34 and abi.block_bytes(abi.Q4_1) == 20
     assert abi.block_bytes(7) == 0
     assert abi.expert_bytes(2048, 512, abi.Q8_0) == 3342336
@@ -70,6 +70,10 @@ def test_host_validation_rejects_before_any_launch():
     assert abi.raw_gather_group([16] * 17, 64, 16, 0, 64, stream=0) == -1        # more than 16 experts
     assert abi.raw_gather_group([16] * 4, 64, 16, 13, 64, stream=0) == -1        # 13 + 4 > 16
     assert abi.raw_gather_group([16, 0], 64, 16, 0, 64, stream=0) == -1          # a null expert pointer
+    assert abi.raw_gather_group_mmq([16] * 2, abi.Q4_1, 256, 128, 16, 0, 64, stream=0) == -1  # stride
+    assert abi.raw_gather_group_mmq([16], abi.Q4_1, 200, 128, 16, 0, 0, stream=0) == -2       # H % 128
+    assert abi.raw_gather_group_mmq([16], 7, 256, 128, 16, 0, 0, stream=0) == -2              # type
+    assert abi.raw_gather_group_mmq([0], abi.Q8_0, 256, 128, 16, 0, 0, stream=0) == -1        # null
     assert abi.raw_mmq_grouped(abi.Q8_0, 16, 256, 0, 128, 128, [0], 16, 4, 16, 3, 16, stream=0) == -1
     assert abi.raw_mmq_grouped(abi.Q8_0, 16, 256, 0, 100, 128, [0], 16, 4, 16, 0, 16, stream=0) == -2
     assert abi.raw_mmq_grouped(abi.Q8_0, 16, 256, 0, 128, 128, [4], 16, 4, 16, 0, 16, stream=0) == -1

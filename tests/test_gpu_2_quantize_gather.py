@@ -92,3 +92,46 @@ def test_gather_batch_equals_per_expert_launches():
     for j in range(16):
         abi.gather_group([ptrs[j]], c.expert_bytes, b, j, c.expert_stride)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("wtype,H,F,misalign", [(synth.Q4_1, 256, 128, 0), (synth.Q8_0, 256, 128, 0),
+                                                (synth.Q8_0, 256, 128, 8), (synth.Q4_1, 256, 128, 8),
+                                                (synth.Q4_1, 384, 256, 3), (synth.Q8_0, 2048, 512, 0),
+                                                (synth.Q4_1, 2048, 512, 0)])
+def test_gather_group_mmq_bytes(orc, wtype, H, F, misalign):
+    """The MMQ-layout gather against the oracle's, byte for byte: batches of 1..16 at several
+    start positions; sources 8-byte (Q4_1) or 1-byte aligned take the byte-wise path."""
+    rng = np.random.default_rng(H + F + misalign + 10 * wtype)
+    eb = abi.expert_bytes(H, F, wtype)
+    E = 18
+    slot = ((eb + 255) // 256) * 256 + 64
+    pool = rng.integers(0, 256, E * slot + 64, dtype=np.uint8)
+    d_pool = dev(pool)
+    base = d_pool.data_ptr()
+    off = (rng.permutation(E) * slot + misalign).astype(np.int64)
+    stride = ((eb + 255) // 256) * 256
+    buf = torch.empty(16 * stride, dtype=torch.uint8, device="cuda")
+    cases = [(1, 0), (3, 13), (16, 0), (7, 4)] if eb < 10 ** 6 else [(16, 0), (2, 14)]
+    for n, first in cases:
+        note(f"gather_mmq wtype={wtype} H={H} F={F} n={n} first={first} misalign={misalign}")
+        experts = rng.choice(E, n, replace=False).astype(np.int32)
+        buf.fill_(0xAB)
+        abi.gather_group_mmq([base + int(off[e]) for e in experts], wtype, H, F, buf, first, stride)
+        got = host(buf)
+        want = np.full(16 * stride, 0xAB, np.uint8)
+        orc.gather_mmq(pool, off, experts, wtype, H, F, want, first, stride)
+        assert np.array_equal(got, want), (n, first)
+
+
+def test_gather_mmq_batch_equals_per_expert_launches():
+    """One MMQ-layout launch for a group equals sixteen one-expert launches, byte for byte."""
+    c = synth.make_case(T=4, H=256, F=128, E=16, K=2, wtype=synth.Q8_0, seed=78)
+    d_pool = dev(c.pool)
+    ptrs = [d_pool.data_ptr() + int(o) for o in c.expert_off]
+    a = torch.zeros(16 * c.expert_stride, dtype=torch.uint8, device="cuda")
+    b = torch.zeros_like(a)
+    note("gather_mmq batch vs per expert")
+    abi.gather_group_mmq(ptrs, c.wtype, c.H, c.F, a, 0, c.expert_stride)
+    for j in range(16):
+        abi.gather_group_mmq([ptrs[j]], c.wtype, c.H, c.F, b, j, c.expert_stride)
+    assert torch.equal(a, b)

@@ -20,11 +20,11 @@ def _setup(orc, wtype, T, H, F, E, K, seed, skew=None):
     idx, _ = orc.route_topk(c.logits, K)
     m = orc.build_maps(idx, E)
     q8x = orc.quantize_scatter(c.x, K, m["slot"])
-    # group buffer: positions 0..n-1 hold experts in a shuffled order
+    # group buffer: positions 0..n-1 hold experts in a shuffled order, in the MMQ layout
     experts = np.random.default_rng(seed).permutation(E)[:min(E, 16)].astype(np.int32)
     stride = c.expert_stride
     gbuf = np.zeros(len(experts) * stride, np.uint8)
-    orc.gather(c.pool, c.expert_off, experts, c.expert_bytes, gbuf, 0, stride)
+    orc.gather_mmq(c.pool, c.expert_off, experts, wtype, H, F, gbuf, 0, stride)
     return c, m, q8x, experts, gbuf
 
 
@@ -54,7 +54,7 @@ def test_mmq_block_dots_bit_exact(orc, wtype, shape):
         r0, r1 = m["offsets"][e], m["offsets"][e + 1]
         if r1 == r0:
             continue
-        wmat = gbuf[j * c.expert_stride:j * c.expert_stride + gu]
+        wmat = c.expert(e)[:gu]          # the raw matrices (the group buffer is repacked)
         want = orc.block_dots(wtype, wmat, 2 * F, H, q8x[r0:r1])
         assert np.array_equal(got[r0:r1], want), (j, e)
     # rows of experts outside the group stay untouched
@@ -84,8 +84,7 @@ def test_mmq_down_f32(orc, wtype, shape):
         r0, r1 = m["offsets"][e], m["offsets"][e + 1]
         if r1 == r0:
             continue
-        wmat = gbuf[j * c.expert_stride + mat_off:j * c.expert_stride + mat_off + H * nb *
-                    synth.BLOCK_BYTES[wtype]]
+        wmat = c.expert(e)[mat_off:mat_off + H * nb * synth.BLOCK_BYTES[wtype]]
         want = orc.mmq_rows(wtype, wmat, H, F, hq8[r0:r1])
         dots = orc.block_dots(wtype, wmat, H, F, hq8[r0:r1])
         bound = _abs_term_bound(wtype, wmat, H, F, hq8[r0:r1], dots) * (nb + 2) * 2.0 ** -23
@@ -109,9 +108,8 @@ def test_mmq_swiglu_q8_1(orc, wtype):
         r0, r1 = m["offsets"][e], m["offsets"][e + 1]
         if r1 == r0:
             continue
-        base = j * c.expert_stride
-        g = orc.mmq_rows(wtype, gbuf[base:base + gu_bytes], F, H, q8x[r0:r1])
-        u = orc.mmq_rows(wtype, gbuf[base + gu_bytes:base + 2 * gu_bytes], F, H, q8x[r0:r1])
+        g = orc.mmq_rows(wtype, c.expert(e)[:gu_bytes], F, H, q8x[r0:r1])
+        u = orc.mmq_rows(wtype, c.expert(e)[gu_bytes:2 * gu_bytes], F, H, q8x[r0:r1])
         h = g / (1.0 + np.exp(-g)) * u
         # the kernel's h: fp32 accumulation of the same products
         assert np.max(np.abs(got_h[r0:r1] - h)) <= 1e-5 * max(np.max(np.abs(h)), 1e-30)
@@ -132,7 +130,7 @@ def test_mmq_group_position_independence(orc):
         perm = np.random.default_rng(perm_seed).permutation(len(experts))
         ex2 = experts[perm]
         gb2 = np.zeros_like(gbuf)
-        orc.gather(c.pool, c.expert_off, ex2, c.expert_bytes, gb2, 0, c.expert_stride)
+        orc.gather_mmq(c.pool, c.expert_off, ex2, wtype, H, F, gb2, 0, c.expert_stride)
         out = torch.zeros((R, abi.q8_1_row_bytes(F)), dtype=torch.uint8, device="cuda")
         note(f"mmq position permutation {perm_seed}")
         abi.mmq_grouped(wtype, dev(gb2), c.expert_stride, 0, F, H, ex2, dev(m["offsets"]), E,
@@ -165,8 +163,7 @@ def test_mmq_down_subnormal_scales(orc, wtype):
         r0, r1 = m["offsets"][e], m["offsets"][e + 1]
         if r1 == r0:
             continue
-        wmat = gbuf[j * c.expert_stride + mat_off:j * c.expert_stride + mat_off + H * nb *
-                    synth.BLOCK_BYTES[wtype]]
+        wmat = c.expert(e)[mat_off:mat_off + H * nb * synth.BLOCK_BYTES[wtype]]
         want = orc.mmq_rows(wtype, wmat, H, F, hq8[r0:r1])
         dots = orc.block_dots(wtype, wmat, H, F, hq8[r0:r1])
         bound = _abs_term_bound(wtype, wmat, H, F, hq8[r0:r1], dots) * (nb + 2) * 2.0 ** -23

@@ -70,7 +70,8 @@ def test_layer_against_oracle(orc, case):
     stride = abi.workspace_offset(abi.WS_GROUP_STRIDE, T, H, F, E, K, wtype, 16)
     groups = region(abi.WS_GROUPS, n * stride).reshape(n, stride)
     for i, e in enumerate(m["order"]):
-        assert np.array_equal(groups[i, :c.expert_bytes], c.expert(e)), (i, e)
+        want = orc.mmq_pack(c.wtype, c.expert(e), c.H, c.F)
+        assert np.array_equal(groups[i, :c.expert_bytes], want), (i, e)
     Dm = region(abi.WS_DM, R * H * 4).view(np.float32).reshape(R, H)
     assert rel_err(Dm, dbg["Dm"]) <= TOL
 

@@ -59,7 +59,7 @@ def test_full_size_workload(orc, name):
     og = abi.workspace_offset(abi.WS_GROUPS, c.T, c.H, c.F, c.E, c.K, c.wtype, 16)
     for i in sorted({0, n // 2, n - 1}):
         got_e = host(ws[og + i * stride:og + i * stride + c.expert_bytes])
-        assert np.array_equal(got_e, c.expert(int(m["order"][i])))
+        assert np.array_equal(got_e, orc.mmq_pack(c.wtype, c.expert(int(m["order"][i])), c.H, c.F))
     # output rows of sampled tokens against the oracle (the GPU's routing as its input)
     ts_out = ts[:24] if len(ts) > 24 else ts
     ts_out = np.unique(np.concatenate([ts_out, np.array(c.zero_tokens, dtype=np.int64)]))

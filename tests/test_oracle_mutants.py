@@ -40,10 +40,20 @@ MUTANTS = {
     "f16_ties_away": ("double m = nearbyint(a * ldexp(1.0, 10 - E));", "double m = floor(a * ldexp(1.0, 10 - E) + 0.5);"),
     "weights_not_renormalised": ("for (int k = 0; k < K; ++k) w[(size_t)t * K + k] = (float)(ex[k] / sum);",
                                  "for (int k = 0; k < K; ++k) w[(size_t)t * K + k] = (float)(ex[k] / (sum + 1.0));"),
-    "gather_position_ignores_first": ("group_buf + (size_t)(first_pos + j) * pos_stride",
-                                      "group_buf + (size_t)j * pos_stride"),
+    "gather_position_ignores_first": ("memcpy(group_buf + (size_t)(first_pos + j) * pos_stride,",
+                                      "memcpy(group_buf + (size_t)j * pos_stride,"),
+    "gather_mmq_position_ignores_first": ("group_buf + (size_t)(first_pos + j) * pos_stride);",
+                                          "group_buf + (size_t)j * pos_stride);"),
     "down_at_up_offset": ("const uint8_t *down = expert + (size_t)2 * F * gu_row;",
                           "const uint8_t *down = expert + (size_t)F * gu_row;"),
+    "mmq_pack_q_shifted": ("memcpy(dst + 16 + 16 * j, src + j * bb + 4, 16);  /* qs */",
+                           "memcpy(dst + 16 + 16 * j, src + j * bb + 3, 16);  /* qs */"),
+    "mmq_pack_d_order": ("memcpy(dst + 2 * j, src + j * bb, 2);             /* d */",
+                         "memcpy(dst + 6 - 2 * j, src + j * bb, 2);         /* d */"),
+    "mmq_pack_tile_rows": ("uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;",
+                           "uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 32) * G;"),
+    "mmq_pack_row_major": ("uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;",
+                           "uint8_t *dst = out + ((size_t)n * stages + t) * G;"),
 }
 
 
@@ -61,6 +71,8 @@ def _pins(orc):
     yield lambda: tr.test_maps_against_brute_force(orc, 64, 4, 32, 31)
     yield lambda: tg.test_gather_is_per_expert_copy(orc)
     for w in W:
+        yield lambda w=w: tg.test_mmq_pack_keeps_every_block(orc, w, 256, 128)
+        yield lambda w=w: tg.test_gather_mmq_positions(orc, w)
         yield lambda w=w: tg.test_block_idot_against_unpacked_integers(orc, w)
         yield lambda w=w: tg.test_row_dot_against_dequantised_fp64(orc, w)
         yield lambda w=w: tl.test_dense_special_case(orc, w)
