@@ -228,6 +228,7 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
     issue_stage<WT>(buf, plan, abase + (size_t)t * kARow, W + (size_t)t * 64 * Geo<WT>::kBRow);
   };
 
+
   // One stage: wait until stage s is in LDS for every wave (which also means every wave is done
   // with stage s-1, whose buffer `fill` then receives stage s+2), then its MFMAs.  The three
   // buffers are distinct LDS objects used with fixed roles per unrolled step, so the compiler
@@ -312,7 +313,12 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
     if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
     if (s0 + 2 < nstages) step(s0 + 2, L2, L1);
   }
-  if (EPI == 2 || !live) return;
+  if (EPI == 2) return;
+  if (EPI == 1) {  // every wavefront is past its last stage: the ring becomes scratch
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (!live) return;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {  // remove the factor 2 of the doubled scales (exact)
     acc0[i] *= 0.5f;
@@ -333,38 +339,57 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
     return;
   }
 
-  // EPI == 1: h = silu(g) * u, then q8_1 along F: the 32 lanes of a half hold one block.
-  // silu uses the hardware exp and reciprocal (h only has to be accurate); the quantisation of
-  // h is the exact q8_1 arithmetic.
-  const int f = n0 + 32 * wc + l32;
-  const int fb = (n0 + 32 * wc) / kQK;  // block index along F
-  const size_t h_row_bytes = (size_t)(p.n_out / kDs4Vals) * kDs4Bytes;
-  const size_t hoff = (size_t)(fb >> 2) * kDs4Bytes;
-  const size_t qoff = hoff + 16 + (fb & 3) * 32 + l32;
-  uint8_t* hq = reinterpret_cast<uint8_t*>(p.out);
+  // EPI == 1: h = silu(g) * u, then q8_1 along F.  A lane holds one feature of 16 rows; the
+  // wavefront's 32 x 32 block of h goes through LDS so that two lanes own one row's block of 32
+  // features (16 each): the block's max and sum then take one exchange between the two lanes,
+  // and each lane stores its 16 q bytes with one 16-byte write.  silu uses the hardware exp and
+  // reciprocal (h only has to be accurate); the quantisation of h is the exact q8_1 arithmetic.
+  float* xs = reinterpret_cast<float*>(&L0) + wave * 32 * 32;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
     const float g = acc0[i], u = acc1[i];
-    const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-    float am = fabsf(h);
+    xs[(8 * (i >> 2) + 4 * half + (i & 3)) * 32 + l32] =
+        g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  const int rr = lane & 31, part = lane >> 5;  // row of the wavefront's 32, 16-feature half
+  float v[16];
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-    const bool nz = am > 0.0f;
-    const float d = am / 127.0f;
-    const int q = nz ? (int)roundf(h / d) : 0;
-    int S = q;
+  for (int k = 0; k < 4; ++k) {
+    const float4 t = *reinterpret_cast<const float4*>(xs + rr * 32 + 16 * part + 4 * k);
+    v[4 * k] = t.x, v[4 * k + 1] = t.y, v[4 * k + 2] = t.z, v[4 * k + 3] = t.w;
+  }
+  float am = 0.0f;
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) S += __shfl_xor(S, off);
-    if (row < nrows) {
-      const size_t r = (size_t)(row0 + row);
-      uint8_t* dst = hq + r * h_row_bytes;
-      dst[qoff] = (uint8_t)(q & 0xff);
-      if (l32 == 0) {
-        const uint32_t hdr = nz ? (f2h(d) | (q8_1_scale_bits(d, S) << 16)) : 0u;
-        *reinterpret_cast<uint32_t*>(dst + hoff + (fb & 3) * 4) = hdr;
-      }
-      if (p.debug_h != nullptr) p.debug_h[r * p.n_out + f] = h;
+  for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(v[k]));
+  am = fmaxf(am, __shfl_xor(am, 32));
+  const bool nz = am > 0.0f;
+  const float d = am / 127.0f;
+  uint32_t qw[4] = {0, 0, 0, 0};
+  int S = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int q = nz ? (int)roundf(v[k] / d) : 0;
+    S += q;
+    qw[k >> 2] |= (uint32_t)(q & 0xff) << (8 * (k & 3));
+  }
+  S += __shfl_xor(S, 32);
+  const int row = 32 * wr + rr;
+  if (row < nrows) {
+    const int fb = (n0 + 32 * wc) / kQK;  // block index along F
+    const size_t h_row_bytes = (size_t)(p.n_out / kDs4Vals) * kDs4Bytes;
+    const size_t hoff = (size_t)(fb >> 2) * kDs4Bytes;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + (size_t)(row0 + row) * h_row_bytes;
+    *reinterpret_cast<uint4*>(dst + hoff + 16 + (fb & 3) * 32 + 16 * part) =
+        make_uint4(qw[0], qw[1], qw[2], qw[3]);
+    if (part == 0) {
+      const uint32_t hdr = nz ? (f2h(d) | (q8_1_scale_bits(d, S) << 16)) : 0u;
+      *reinterpret_cast<uint32_t*>(dst + hoff + (fb & 3) * 4) = hdr;
+    }
+    if (p.debug_h != nullptr) {
+      float* dh = p.debug_h + (size_t)(row0 + row) * p.n_out + n0 + 32 * wc + 16 * part;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dh[k] = v[k];
     }
   }
 }
