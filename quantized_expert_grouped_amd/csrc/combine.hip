@@ -5,13 +5,18 @@
 // token's own rows).
 //
 // One workgroup per token; each thread owns float4 columns of the row, reads the K routed rows
-// with 16-byte loads and writes the output once.
+// with 16-byte loads, up to 8 rows' loads in flight before their fused multiply-adds, and
+// writes the output once.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
 namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBatchK = 8;  // routed rows whose loads are in flight together
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Dm,
                                                       const int32_t* __restrict__ slot,
@@ -27,16 +32,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __syncthreads();
   const int n4 = H / 4;
   for (int c = threadIdx.x; c < n4; c += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      const float4 d = reinterpret_cast<const float4*>(Dm + (size_t)s_row[k] * H)[c];
-      const float wk = s_w[k];
-      acc.x = fmaf(wk, d.x, acc.x);
-      acc.y = fmaf(wk, d.y, acc.y);
-      acc.z = fmaf(wk, d.z, acc.z);
-      acc.w = fmaf(wk, d.w, acc.w);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += kBatchK) {
+      // the loads of up to kBatchK rows first (each row is read once: non-temporal), then the
+      // fused multiply-adds in k order
+      v4f d[kBatchK];
+#pragma unroll
+      for (int j = 0; j < kBatchK; ++j)
+        if (k0 + j < K)
+          d[j] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4f*>(Dm + (size_t)s_row[k0 + j] * H) + c);
+#pragma unroll
+      for (int j = 0; j < kBatchK; ++j) {
+        if (k0 + j < K) {
+          const float wk = s_w[k0 + j];
+          acc.x = fmaf(wk, d[j].x, acc.x);
+          acc.y = fmaf(wk, d[j].y, acc.y);
+          acc.z = fmaf(wk, d[j].z, acc.z);
+          acc.w = fmaf(wk, d[j].w, acc.w);
+        }
+      }
     }
-    reinterpret_cast<float4*>(out + (size_t)t * H)[c] = acc;
+    __builtin_nontemporal_store(acc, reinterpret_cast<v4f*>(out + (size_t)t * H) + c);
   }
 }
 

@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_all_kernel(
 // The expert keeps its order (gate | up | down) and its size.  A 64-row tile is one contiguous
 // run in the raw expert and one in the packed expert, so a workgroup moves a tile's rows for
 // up to kPackStages stages: it reads the rows' bytes into LDS with wide coalesced loads and
-// writes the tile-stages out, also coalesced, picking each output word from LDS.
+// writes the tile-stages out, also coalesced, picking each output word from LDS.  Both the
+// pool reads and the packed writes are non-temporal: each byte is moved once.
 
 constexpr int kPackStages = 4;
 
@@ -175,7 +176,7 @@ __device__ __forceinline__ void pack_item(const uint8_t* __restrict__ src_e,
       v[u] = packed_word<WT>(lds + i * seg + st * G, k);
     }
     if (wide) {
-      reinterpret_cast<v4u*>(d)[q] = (v4u){v[0], v[1], v[2], v[3]};
+      __builtin_nontemporal_store((v4u){v[0], v[1], v[2], v[3]}, reinterpret_cast<v4u*>(d) + q);
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
