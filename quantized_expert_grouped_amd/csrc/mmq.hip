@@ -177,6 +177,24 @@ __device__ __forceinline__ v4i b_frag(const uint8_t* brow, int b, int half) {
   return (v4i){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
 }
 
+// The same operand in two steps, so that the LDS read can run ahead: the raw bytes (Q4_1: the
+// 8 packed bytes in the low two words), then the int8 operand.
+template <int WT>
+__device__ __forceinline__ v4i b_raw(const uint8_t* brow, int b, int half) {
+  if (WT == 1) {
+    const uint2 x = *reinterpret_cast<const uint2*>(brow + 16 + 16 * b + 8 * half);
+    return (v4i){(int)x.x, (int)x.y, 0, 0};
+  }
+  return b_frag<WT>(brow, b, half);
+}
+
+template <int WT>
+__device__ __forceinline__ v4i b_unpack(const v4i& r) {
+  if (WT == 0) return r;
+  const uint32_t m = 0x0f0f0f0fu, x0 = (uint32_t)r[0], x1 = (uint32_t)r[1];
+  return (v4i){(int)(x0 & m), (int)(x1 & m), (int)((x0 >> 4) & m), (int)((x1 >> 4) & m)};
+}
+
 // The f16 MFMA operand of a row's weight headers: Q4_1 (d_b, m_b) in fp16 slots 2b, 2b+1;
 // Q8_0 d_b in slot b (slots 4..7 zero).
 template <int WT>
@@ -272,13 +290,19 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
     const v4i hx = *reinterpret_cast<const v4i*>(arow);
     const v8h hw0 = __builtin_bit_cast(v8h, b_header<WT>(brow0));
     const v8h hw1 = __builtin_bit_cast(v8h, b_header<WT>(brow1));
+    // the LDS reads of each block's operands are issued one block ahead of its MFMAs
+    v4i fa = a_frag<WT>(arow, 0, half), f0 = b_raw<WT>(brow0, 0, half),
+        f1 = b_raw<WT>(brow1, 0, half);
 #pragma unroll
     for (int b = 0; b < kKB; ++b) {
-      const v4i a = a_frag<WT>(arow, b, half);
-      const v16i I0 =
-          __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow0, b, half), izero, 0, 0, 0);
-      const v16i I1 =
-          __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_frag<WT>(brow1, b, half), izero, 0, 0, 0);
+      const v4i a = fa, x0 = f0, x1 = f1;
+      if (b + 1 < kKB) {
+        fa = a_frag<WT>(arow, b + 1, half);
+        f0 = b_raw<WT>(brow0, b + 1, half);
+        f1 = b_raw<WT>(brow1, b + 1, half);
+      }
+      const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x0), izero, 0, 0, 0);
+      const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x1), izero, 0, 0, 0);
       // 2 * dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero)
       if (WT == 1)
         za[b][b] = (int)((uint32_t)hx[b] & 0xffffu);
