@@ -207,9 +207,19 @@ __global__ __launch_bounds__(kGatherThreads) void gather_mmq_all_kernel(
     const int32_t* __restrict__ order, const int32_t* __restrict__ n_active, int H, int F,
     uint8_t* __restrict__ dst, size_t stride) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[Pack<WT>::kLds];
-  const int pos = blockIdx.z * gridDim.y + blockIdx.y;
+  // Workgroups reach the 8 XCDs round-robin; renumber them so that each XCD moves a contiguous
+  // run of (expert, item) pairs, keeping the neighbouring slices of a tile, which share cache
+  // lines at their edges, in one L2.  (blockIdx.z = group and blockIdx.y = position in it, as
+  // in one group's launch.)
+  const int items = gridDim.x;
+  const int n = items * gridDim.y * gridDim.z;
+  const int id = blockIdx.x + items * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = id % 8;
+  const int work = xcd * (n / 8) + min(xcd, n % 8) + id / 8;
+  const int pos = work / items;
   if (pos >= *n_active) return;
-  pack_item<WT>(pool + expert_off[order[pos]], dst + (size_t)pos * stride, H, F, blockIdx.x, lds);
+  pack_item<WT>(pool + expert_off[order[pos]], dst + (size_t)pos * stride, H, F, work % items,
+                lds);
 }
 
 int parts_for(size_t bytes) {
