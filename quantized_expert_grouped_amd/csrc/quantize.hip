@@ -37,11 +37,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   if (MODE == 0) my_row = lane < K ? slot[(size_t)t * K + lane] : 0;
   const int nrows = MODE == 0 ? K : 1;
 
-  for (int c0 = 0; c0 < H; c0 += 64 * 16) {
+  // The row is taken in chunks of 1024 values (16 per lane), two chunks' loads in flight at a
+  // time so that the second chunk's latency overlaps the first's quantisation and stores.
+  auto load = [&](int c0, float* v) {
     const int v0 = c0 + lane * 16;
-    const bool act = v0 < H;  // H is a multiple of 128: whole 8-lane groups
-    float v[16];
-    if (act) {
+    if (v0 < H) {  // H is a multiple of 128: whole 8-lane groups
       const float4* p = reinterpret_cast<const float4*>(xr + v0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -55,6 +55,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = 0.0f;
     }
+  };
+  auto quantize_chunk = [&](int c0, const float* v) {
+    const int v0 = c0 + lane * 16;
+    const bool act = v0 < H;
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
@@ -92,6 +96,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
         if ((lane & 7) == 0) *reinterpret_cast<uint4*>(row + hoff) = hv;
       }
     }
+  };
+  for (int c0 = 0; c0 < H; c0 += 2 * 64 * 16) {
+    float va[16], vb[16];
+    load(c0, va);
+    const bool second = c0 + 64 * 16 < H;
+    if (second) load(c0 + 64 * 16, vb);
+    quantize_chunk(c0, va);
+    if (second) quantize_chunk(c0 + 64 * 16, vb);
   }
 }
 
