@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_GROUP 16     /* experts per group buffer ([G1] "What": MMQ_GROUP = 16) */
 #define MOE_MAX_E 2048       /* largest expert count the kernels accept */
 #define MOE_MAX_K 64         /* largest routes per token */
@@ -184,6 +184,91 @@ enum {
 };
 size_t moe_workspace_offset(int which, int T, int H, int F, int E, int K, int wtype,
                             int group_size);
+
+/* ---- Streamed walk ([G2] "What changes"; the per-expert form it replaces: the opening section) ----
+ *
+ * Experts that are not resident in device memory are copied from a host arena into a ring of
+ * device slots on a copy stream, while the compute stream walks the routed experts in ring order.
+ * Per gather batch (at most one group of group_size positions):
+ *   - one wait: the compute stream waits on an event recorded after the batch's last copy (the
+ *     copy stream is in order, so that covers every copy of the batch);
+ *   - one launch: moe_gather_group_mmq's kernel moves the batch's experts (ring slots or resident
+ *     experts) to their group buffer positions;
+ *   - one event: recorded after that launch, it gives every ring slot the batch read back to the
+ *     copies: before a slot is refilled the copy stream waits on used[used_of[slot]], used_of
+ *     mapping each slot to the event recorded by the last batch that read it (events are reused
+ *     round-robin from a pool of MOE_WALK_EVENTS: an event recorded again by a later batch can
+ *     only delay such a copy, never let it start early).
+ * A batch is launched when its group is complete, when the walk meets a ring entry the routing
+ * skipped while the group is open ([G2] "What changes": the entries waiting in an open batch
+ * never exceed one group), or when the next copy needs a ring slot that the open batch itself holds (a ring
+ * smaller than a group).  After a group's last batch its MMQ gate/up and down launch on that
+ * group's m-tiles, so a group's products overlap later groups' copies.  The output is
+ * bit-identical to moe_prefill_layer's for the same arguments (the same bytes reach the same
+ * positions; the products and their order are unchanged). */
+#define MOE_WALK_EVENTS 64
+#define MOE_WALK_GATHER_ONE 1      /* one expert per batch: one wait, launch and event per expert
+                                      ([G2] "What changes", the opt-out) */
+#define MOE_WALK_NO_SKIP_FLUSH 2   /* a skipped ring entry does not launch the open batch */
+
+typedef struct moe_walk moe_walk;
+
+/* Creates the walk's state for a caller-owned device ring of n_slots (>= 1) slots, slot_stride
+ * bytes apart (a multiple of 256): a copy stream (default priority), MOE_WALK_EVENTS + 2 events,
+ * a pinned host buffer for the routing read-back, and the slot map (every slot free).  The ring
+ * must stay allocated until moe_walk_destroy.  *walk is set on MOE_OK. */
+int moe_walk_create(void *ring, int n_slots, size_t slot_stride, moe_walk **walk);
+
+/* Waits for the walk's copy stream, then frees what moe_walk_create made.  NULL is a no-op. */
+int moe_walk_destroy(moe_walk *walk);
+
+/* The whole layer as moe_prefill_layer computes it, with the experts streamed as described above.
+ *   host_arena [host, pinned]: arena_bytes bytes; host_off [host] int64 [E]: expert e's raw bytes
+ *     start at host_arena + host_off[e];
+ *   resident [host] [E]: a device pointer to expert e's raw bytes, or NULL to stream it;
+ *   flags: MOE_WALK_* bits.
+ * Other arguments as in moe_prefill_layer (same workspace, moe_workspace_size).  The call blocks
+ * the host once, until the routing is known on the host (the maps, then a read-back of counts,
+ * order and n_active: the routing sync); everything after it is enqueued on `stream` and the
+ * walk's copy stream.  The arena must stay unchanged until `stream` has passed this call.
+ * Calls on one walk must not overlap; the walk's slot map and events carry over between calls,
+ * so a slot read by one call is refilled by the next only after that read. */
+/* After a MOE_EHIP from this call the walk's slot map may name events that were never recorded:
+ * destroy the walk. */
+int moe_prefill_layer_streamed(moe_walk *walk, const float *x, int T, int H, int F, int E, int K,
+                               const int32_t *topk_idx, const float *topk_w, int wtype,
+                               const void *host_arena, size_t arena_bytes,
+                               const int64_t *host_off, const void *const *resident,
+                               int group_size, int ring_start, int flags, void *ws,
+                               size_t ws_bytes, float *out, void *stream);
+
+/* Counters of a walk since it was created [host] int64 [n]:
+ *   0 copies, 1 bytes copied, 2 gather batches, 3 compute-stream waits on copies,
+ *   4 copy-stream waits on slot events, 5 batches launched for a skipped entry,
+ *   6 batches launched for a ring slot held by the open batch, 7 MMQ launches, 8 routing syncs.
+ * Writes min(n, MOE_WALK_NSTATS) entries. */
+#define MOE_WALK_NSTATS 9
+int moe_walk_stats(const moe_walk *walk, int64_t *stats, int n);
+
+/* The walk's schedule alone, computed on the host as moe_prefill_layer_streamed computes it
+ * (nothing is enqueued; no device is needed).  Inputs [host]: counts int32 [E], order int32 [E]
+ * and n_active as moe_build_maps returns them; streamed uint8 [E] (1 = copied from the arena);
+ * group_size, n_slots, flags as above.  State in/out [host]: used_of int32 [n_slots] (the event
+ * of each slot's last reader batch, -1 = never read), cursor (next ring slot, 0..n_slots-1),
+ * next_event (the event the next batch records, 0..MOE_WALK_EVENTS-1).  ops [host] int32 [max_ops x 6],
+ * one record per step in issue order:
+ *   {1, pos, expert, slot, wait_event (-1: none), 0}         copy expert into a ring slot
+ *   {2, first_pos, n, waits (0/1), event, why}               gather batch of positions
+ *                                                            first_pos .. first_pos+n-1;
+ *                                                            why: 0 group complete, 1 skipped
+ *                                                            entry, 2 slot held, 3 one expert
+ *   {3, group, first_pos, n, 0, 0}                           MMQ of the group's positions
+ * Returns the number of records, MOE_EINVAL (inconsistent inputs) or MOE_EWORKSPACE (max_ops too
+ * small; the state is then unspecified). */
+int moe_walk_plan(const int32_t *counts, const int32_t *order, int n_active, int E,
+                  int ring_start, const uint8_t *streamed, int group_size, int n_slots, int flags,
+                  int32_t *used_of, int32_t *cursor, int32_t *next_event, int32_t *ops,
+                  int max_ops);
 
 /* Optional stage timing of moe_prefill_layer with HIP events recorded on the call's stream.
  * moe_profile_begin(n) arms it for the next n calls (creates the events); moe_profile_end()

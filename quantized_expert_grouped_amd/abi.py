@@ -22,6 +22,13 @@ WS_COUNTS, WS_OFFSETS, WS_SRC, WS_SLOT, WS_ORDER, WS_NACTIVE, WS_Q8X, WS_GROUPS,
 N_STAGES = 6
 STAGES = ("maps", "quantize", "gather", "gate_up", "down", "combine")
 
+WALK_EVENTS = 64
+WALK_GATHER_ONE, WALK_NO_SKIP_FLUSH = 1, 2
+WALK_NSTATS = 9
+WALK_STATS = ("copies", "bytes", "batches", "waits", "copy_waits", "skip_flushes", "slot_flushes",
+              "mmq_launches", "routing_syncs")
+OP_COPY, OP_GATHER, OP_MMQ = 1, 2, 3
+
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EWORKSPACE",
           -4: "MOE_EHIP"}
 
@@ -44,6 +51,12 @@ SIGNATURES = {
     "moe_combine": (I, [P, P, P, I, I, I, P, P]),
     "moe_prefill_layer": (I, [P, I, I, I, I, I, P, P, I, P, P, SZ, I, I, P, SZ, P, P]),
     "moe_workspace_offset": (SZ, [I, I, I, I, I, I, I, I]),
+    "moe_walk_create": (I, [P, I, SZ, P]),
+    "moe_walk_destroy": (I, [P]),
+    "moe_prefill_layer_streamed": (I, [P, P, I, I, I, I, I, P, P, I, P, SZ, P, P, I, I, I, P, SZ,
+                                       P, P]),
+    "moe_walk_stats": (I, [P, P, I]),
+    "moe_walk_plan": (I, [P, P, I, I, I, P, I, I, I, P, P, P, P, I]),
     "moe_profile_begin": (I, [I]),
     "moe_profile_end": (I, [P, I]),
 }
@@ -220,3 +233,84 @@ def profile_end(max_calls: int) -> np.ndarray:
     if n < 0:
         raise MoeError("moe_profile_end", n)
     return ms[:n]
+
+
+# ---- streamed walk --------------------------------------------------------------------------
+class Walk:
+    """A walk's state (copy stream, events, slot map) over a caller-owned device ring of n_slots
+    slots of slot_stride bytes (`ring`: a device tensor kept alive by this object)."""
+
+    def __init__(self, ring, n_slots: int, slot_stride: int):
+        self.ring = ring
+        self.n_slots, self.slot_stride = n_slots, slot_stride
+        h = ctypes.c_void_p()
+        _check("moe_walk_create", lib().moe_walk_create(_ptr(ring), n_slots, slot_stride,
+                                                        ctypes.byref(h)))
+        self.handle = h.value
+
+    def close(self) -> None:
+        if self.handle:
+            lib().moe_walk_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def stats(self) -> dict:
+        a = np.zeros(WALK_NSTATS, np.int64)
+        _check("moe_walk_stats", lib().moe_walk_stats(self.handle,
+                                                      a.ctypes.data_as(ctypes.c_void_p),
+                                                      WALK_NSTATS))
+        return dict(zip(WALK_STATS, (int(v) for v in a)))
+
+
+def raw_prefill_layer_streamed(walk, x, topk_idx, topk_w, wtype, host_arena, host_off, resident,
+                               F, E, group_size, ring_start, flags, ws, out, stream=None,
+                               arena_bytes=None):
+    """host_arena: a pinned host tensor (uint8); host_off: int64 [E]; resident: E device pointers
+    (0 = stream the expert from the arena)."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    off = np.ascontiguousarray(host_off, dtype=np.int64)
+    res = (ctypes.c_void_p * E)(*[int(p) if p else None for p in resident])
+    nb = (host_arena.numel() * host_arena.element_size() if arena_bytes is None
+          else arena_bytes) if host_arena is not None else 0
+    return lib().moe_prefill_layer_streamed(
+        walk.handle if isinstance(walk, Walk) else walk, _ptr(x), T, H, F, E, K, _ptr(topk_idx),
+        _ptr(topk_w), wtype, _ptr(host_arena), nb, off.ctypes.data_as(ctypes.c_void_p),
+        ctypes.cast(res, ctypes.c_void_p), group_size, ring_start, flags, _ptr(ws),
+        ws.numel() * ws.element_size(), _ptr(out), _stream(stream))
+
+
+def prefill_layer_streamed(*args, **kw):
+    _check("moe_prefill_layer_streamed", raw_prefill_layer_streamed(*args, **kw))
+
+
+def walk_plan(counts, order, n_active, ring_start, streamed, group_size, n_slots, flags=0,
+              state=None, max_ops=None):
+    """The walk's schedule (host only).  state: dict with used_of / cursor / next_event, updated
+    in place (a fresh one when None).  Returns (status_or_count, ops int32 [n x 6], state)."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    E = len(counts)
+    order = np.ascontiguousarray(order, dtype=np.int32)
+    if len(order) < E:
+        order = np.concatenate([order, np.zeros(E - len(order), np.int32)])
+    streamed = np.ascontiguousarray(streamed, dtype=np.uint8)
+    if state is None:
+        state = {"used_of": np.full(n_slots, -1, np.int32), "cursor": 0, "next_event": 0}
+    used_of = state["used_of"]
+    cur = ctypes.c_int32(state["cursor"])
+    nev = ctypes.c_int32(state["next_event"])
+    if max_ops is None:
+        max_ops = 4 * E + 8
+    ops = np.zeros((max(max_ops, 1), 6), np.int32)
+    vp = ctypes.c_void_p
+    n = lib().moe_walk_plan(counts.ctypes.data_as(vp), order.ctypes.data_as(vp), n_active, E,
+                            ring_start, streamed.ctypes.data_as(vp), group_size, n_slots, flags,
+                            used_of.ctypes.data_as(vp), ctypes.byref(cur), ctypes.byref(nev),
+                            ops.ctypes.data_as(vp), max_ops)
+    state["cursor"], state["next_event"] = cur.value, nev.value
+    return n, (ops[:n] if n >= 0 else ops[:0]), state

@@ -19,8 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_prefill.so")
 
-SOURCES = ["api.cpp", "route.hip", "maps.hip", "quantize.hip", "gather.hip", "mmq.hip",
-           "combine.hip"]
+SOURCES = ["api.cpp", "walk.cpp", "route.hip", "maps.hip", "quantize.hip", "gather.hip",
+           "mmq.hip", "combine.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

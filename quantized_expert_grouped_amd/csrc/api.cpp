@@ -7,54 +7,12 @@
 #include <vector>
 
 #include "internal.hpp"
+#include "layout.hpp"
 #include "moe_prefill.h"
 
 namespace {
 
 using namespace moe;
-
-inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
-inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
-inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
-
-bool valid_wtype(int wt) { return wt == MOE_Q8_0 || wt == MOE_Q4_1; }
-
-// Region offsets of the layer's workspace (each 256-byte aligned).
-struct Layout {
-  size_t hist, counts, offsets, src, slot, order, nactive, ntiles, tiles, q8x, groups, hq8, dm;
-  size_t group_stride, total;
-  int max_tiles;
-};
-
-bool make_layout(int T, int H, int F, int E, int K, int wt, Layout* L) {
-  if (T < 1 || K < 1 || E < 1 || H < 128 || F < 128 || !valid_wtype(wt)) return false;
-  const size_t R = (size_t)T * K;
-  const size_t eb = moe_expert_bytes(H, F, wt);
-  size_t o = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = o;
-    o = align_up(o + bytes, 256);
-    return at;
-  };
-  L->hist = take((size_t)map_chunks((int)R) * E * 4);
-  L->counts = take((size_t)E * 4);
-  L->offsets = take((size_t)(E + 1) * 4);
-  L->src = take(R * 4);
-  L->slot = take(R * 4);
-  L->order = take((size_t)E * 4);
-  L->nactive = take(4);
-  L->ntiles = take(4);
-  L->max_tiles = max_mtiles((int)R, E, kMmqRows);
-  L->tiles = take((size_t)L->max_tiles * sizeof(MTile));
-  L->q8x = take(R * moe_q8_1_row_bytes(H));
-  L->group_stride = align_up(eb, 256);
-  L->groups = take((size_t)E * L->group_stride);
-  L->hq8 = take(R * moe_q8_1_row_bytes(F));
-  L->dm = take(R * (size_t)H * 4);
-  L->total = o;
-  return true;
-}
 
 // ---- opt-in stage profiler -------------------------------------------------------------------
 constexpr int kEvPerCall = MOE_N_STAGES + 1;
@@ -238,19 +196,11 @@ int moe_prefill_layer(const float* x, int T, int H, int F, int E, int K, const i
                       const float* topk_w, int wtype, const void* pool, const int64_t* expert_off,
                       size_t expert_bytes, int group_size, int ring_start, void* ws,
                       size_t ws_bytes, float* out, void* stream) {
-  if (!x || !topk_idx || !topk_w || !pool || !expert_off || !ws || !out) return MOE_EINVAL;
-  if (T < 1 || K < 1 || E < 1 || K > E || group_size < 1 || group_size > MOE_MAX_GROUP ||
-      ring_start < 0 || ring_start >= E)
-    return MOE_EINVAL;
-  if (!valid_wtype(wtype)) return MOE_EUNSUPPORTED;
-  if (H < 128 || H % 128 != 0 || F < 128 || F % 128 != 0 || E > MOE_MAX_E || K > MOE_MAX_K)
-    return MOE_EUNSUPPORTED;
-  if ((long long)T * K > (1LL << 30)) return MOE_EUNSUPPORTED;
-  if (expert_bytes != moe_expert_bytes(H, F, wtype)) return MOE_EINVAL;
-  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256)) return MOE_EINVAL;
+  if (!pool || !expert_off) return MOE_EINVAL;
   Layout L;
-  if (!make_layout(T, H, F, E, K, wtype, &L)) return MOE_EINVAL;
-  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  const int rc = check_layer_args(x, T, H, F, E, K, topk_idx, topk_w, wtype, expert_bytes,
+                                  group_size, ring_start, ws, ws_bytes, out, &L);
+  if (rc != MOE_OK) return rc;
 
   hipStream_t s = as_stream(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);

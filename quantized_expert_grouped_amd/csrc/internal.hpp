@@ -80,10 +80,12 @@ struct MmqProblem {
   const uint8_t* act;     // q8_1 rows of k_in values
   void* out;
   float* debug_h;
-  // layer form: device tile list
+  // layer form: device tile list; tile_count > 0 takes that many tiles from `tiles` (a count
+  // the host knows), otherwise *n_tiles of them with a grid sized for max_tiles
   const MTile* tiles;
   const int32_t* n_tiles;
   int max_tiles;
+  int tile_count;
   // group form: positions j < n_group hold experts[j], rows from offsets
   const int32_t* offsets;
   int experts[16];

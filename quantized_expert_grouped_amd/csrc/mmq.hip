@@ -428,7 +428,7 @@ template <int WT, int EPI>
 __global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
   __shared__ StageBuf<WT> L0, L1, L2;
   const int ntl = gridDim.x;
-  const int live = ntl * *p.n_tiles;
+  const int live = ntl * (p.tile_count > 0 ? p.tile_count : *p.n_tiles);
   const int id = blockIdx.x + ntl * blockIdx.y;
   if (id >= live) return;
 #ifdef MOE_MMQ_NO_XCD_ORDER
@@ -459,7 +459,7 @@ template <int WT, int EPI>
 hipError_t launch_typed(const MmqProblem& p, hipStream_t s) {
   const int ntiles = EPI == 1 ? p.n_out / 64 : p.n_out / kRowsN;
   if (p.tiles != nullptr) {
-    const dim3 grid(ntiles, p.max_tiles);
+    const dim3 grid(ntiles, p.tile_count > 0 ? p.tile_count : p.max_tiles);
     mmq_layer_kernel<WT, EPI><<<grid, 256, 0, s>>>(p);
   } else {
     const dim3 grid(ntiles, 16, p.n_group);

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert abi.abi_version() == 2
+    assert abi.abi_version() == 3
     assert abi.block_bytes(abi.Q8_0) == 34 and abi.block_bytes(abi.Q4_1) == 20
     assert abi.block_bytes(7) == 0
     assert abi.expert_bytes(2048, 512, abi.Q8_0) == 3342336
@@ -109,3 +109,17 @@ def test_host_validation_rejects_before_any_launch():
 
 def test_profiler_end_without_begin_is_empty():
     assert abi.profile_end(4).shape == (0, abi.N_STAGES)
+
+
+def test_walk_host_validation():
+    L = abi.lib()
+    import ctypes as ct
+    h = ct.c_void_p()
+    assert L.moe_walk_create(None, 4, 256, ct.byref(h)) == -1           # no ring
+    assert L.moe_walk_create(256, 0, 256, ct.byref(h)) == -1            # no slots
+    assert L.moe_walk_create(256, 4, 300, ct.byref(h)) == -1            # stride % 256
+    assert L.moe_walk_create(256, 4, 256, None) == -1                   # nowhere to put it
+    assert L.moe_walk_destroy(None) == 0
+    assert L.moe_walk_stats(None, None, 0) == -1
+    assert L.moe_prefill_layer_streamed(None, 16, 4, 256, 128, 8, 2, 16, 16, 0, 16, 1 << 20, 16,
+                                        16, 16, 0, 0, 16, 1 << 20, 16, None) == -1
