@@ -142,6 +142,91 @@ def cpu_baseline(c, idx, w, target_s: float = 12.0):
                       f"in {dt:.2f} s on {threads} threads"}
 
 
+PEAK_PCIE_GBS = 64.0           # PCIe 5.0 x16, one direction, GB/s
+
+
+def h2d_probe(mib: int, dev) -> float:
+    """GB/s of one plain pinned-host -> device copy of `mib` MiB (the practical PCIe rate)."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(3):
+        t0 = time.perf_counter()
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        best = max(best, (mib << 20) / (time.perf_counter() - t0) / 1e9)
+    return best
+
+
+def streamed_walk(args, c, layer, x, logits, out, dev):
+    """Steps of routing + moe_prefill_layer_streamed; prints one JSON line."""
+    import torch
+    stride = abi.workspace_offset(abi.WS_GROUP_STRIDE, c.T, c.H, c.F, c.E, c.K, c.wtype, 16)
+    # the host arena holds the experts by id, one slot stride apart (as a model loader lays
+    # them out), so a batch's run of consecutive experts can go out as one transfer
+    by_id = np.zeros(c.E * stride, np.uint8)
+    for e in range(c.E):
+        by_id[e * stride:e * stride + c.expert_bytes] = c.expert(e)
+    arena = torch.from_numpy(by_id).pin_memory()
+    host_off = np.arange(c.E, dtype=np.int64) * stride
+    ring = torch.empty(args.ring_slots * stride, dtype=torch.uint8, device=dev)
+    walk = abi.Walk(ring, args.ring_slots, stride)
+    n_res = int(round(args.resident_frac * c.E))
+    keep = set(np.random.default_rng(7).permutation(c.E)[:n_res].tolist())
+    base = layer.pool.data_ptr()
+    resident = [base + int(c.expert_off[e]) if e in keep else 0 for e in range(c.E)]
+    flags = abi.WALK_GATHER_ONE if args.gather_one else 0
+    G = args.walk_group_size
+
+    def step():
+        idx, w = layer.route(logits)
+        abi.prefill_layer_streamed(walk, x, idx, w, c.wtype, arena, host_off, resident, c.F,
+                                   c.E, G, c.ring_start, flags, layer.ws, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st0 = walk.stats()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st1 = walk.stats()
+    d = {k: (st1[k] - st0[k]) / args.steps for k in st1}
+    pcie = h2d_probe(1024, dev)
+    walk.close()
+    ms_per_step = elapsed * 1e3 / args.steps
+    h2d = d["bytes"] / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": "routed rows/sec (TxK) for the MoE prefill layer, streamed experts",
+        "value": round(c.T * c.K * args.steps / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}", "walk": "streamed",
+                   "ring_slots": args.ring_slots, "resident_experts": n_res,
+                   "group_size": G, "gather_one": bool(args.gather_one)},
+        "roofline": {"kernel": "host->device expert copies (copy stream)", "bound": "pcie",
+                     "achieved": round(h2d, 2), "peak": PEAK_PCIE_GBS, "unit": "GB/s",
+                     "frac": round(h2d / PEAK_PCIE_GBS, 4), "traffic": None,
+                     "h2d_probe_gbs": round(pcie, 2)},
+        "per_step": {k: round(v, 1) for k, v in d.items()},
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +239,17 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the steps (counter "
                          "calibration; outside the timed region)")
+    ap.add_argument("--walk", choices=["resident", "streamed"], default="resident",
+                    help="resident: every expert in HBM, the layer's one-launch schedule; "
+                         "streamed: moe_prefill_layer_streamed, experts copied from a pinned "
+                         "host arena through a ring of device slots (another line, not the "
+                         "headline)")
+    ap.add_argument("--ring-slots", type=int, default=96)
+    ap.add_argument("--resident-frac", type=float, default=0.0,
+                    help="streamed walk: the fraction of experts held in HBM (not copied)")
+    ap.add_argument("--walk-group-size", type=int, default=16)
+    ap.add_argument("--gather-one", action="store_true",
+                    help="streamed walk: one gather launch, wait and event per expert")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -176,6 +272,10 @@ def main():
     stream = torch.cuda.current_stream()
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, dev)
+
+    if args.walk == "streamed":
+        streamed_walk(args, c, layer, x, logits, out, dev)
+        return
 
     for _ in range(args.warmup):
         layer.step(x, logits, out)

@@ -244,10 +244,13 @@ int moe_prefill_layer_streamed(moe_walk *walk, const float *x, int T, int H, int
 
 /* Counters of a walk since it was created [host] int64 [n]:
  *   0 copies, 1 bytes copied, 2 gather batches, 3 compute-stream waits on copies,
- *   4 copy-stream waits on slot events, 5 batches launched for a skipped entry,
- *   6 batches launched for a ring slot held by the open batch, 7 MMQ launches, 8 routing syncs.
+ *   4 copy-stream waits on slot events (none is issued for an event already complete),
+ *   5 batches launched for a skipped entry,
+ *   6 batches launched for a ring slot held by the open batch, 7 MMQ launches, 8 routing syncs,
+ *   9 host->device transfers (consecutive copies of one batch whose experts lie slot_stride apart
+ *     in the arena and land in consecutive slots go out as one transfer).
  * Writes min(n, MOE_WALK_NSTATS) entries. */
-#define MOE_WALK_NSTATS 9
+#define MOE_WALK_NSTATS 10
 int moe_walk_stats(const moe_walk *walk, int64_t *stats, int n);
 
 /* The walk's schedule alone, computed on the host as moe_prefill_layer_streamed computes it

@@ -24,9 +24,9 @@ STAGES = ("maps", "quantize", "gather", "gate_up", "down", "combine")
 
 WALK_EVENTS = 64
 WALK_GATHER_ONE, WALK_NO_SKIP_FLUSH = 1, 2
-WALK_NSTATS = 9
+WALK_NSTATS = 10
 WALK_STATS = ("copies", "bytes", "batches", "waits", "copy_waits", "skip_flushes", "slot_flushes",
-              "mmq_launches", "routing_syncs")
+              "mmq_launches", "routing_syncs", "transfers")
 OP_COPY, OP_GATHER, OP_MMQ = 1, 2, 3
 
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EWORKSPACE",

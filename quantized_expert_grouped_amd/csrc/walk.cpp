@@ -29,7 +29,7 @@ enum { kOpCopy = 1, kOpGather = 2, kOpMmq = 3 };
 enum { kWhyGroup = 0, kWhySkip = 1, kWhySlot = 2, kWhyOne = 3 };
 enum {
   kStCopies, kStBytes, kStBatches, kStWaits, kStCopyWaits, kStSkipFlush, kStSlotFlush, kStMmq,
-  kStSyncs
+  kStSyncs, kStTransfers
 };
 
 struct Op {
@@ -272,19 +272,38 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
   dn.out = base + L.dm;
 
   const uint8_t* arena = static_cast<const uint8_t*>(host_arena);
-  for (const Op& op : w.ops) {
-    const int32_t* v = op.v;
+  const size_t nops = w.ops.size();
+  for (size_t k = 0; k < nops; ++k) {
+    const int32_t* v = w.ops[k].v;
     if (v[0] == kOpCopy) {
-      if (v[4] >= 0) {
-        if (!ok(hipStreamWaitEvent(w.copy, w.used[v[4]], 0))) return MOE_EHIP;
-        ++w.stats[kStCopyWaits];
+      // Consecutive copies (always of one batch: a gather record separates batches) whose
+      // experts lie slot_stride apart in the arena and whose slots follow each other go out as
+      // one transfer: the copy engine's cost per transfer is then paid once per run.
+      size_t r = k;
+      while (r + 1 < nops && w.ops[r + 1].v[0] == kOpCopy &&
+             w.ops[r + 1].v[3] == w.ops[r].v[3] + 1 &&
+             host_off[w.ops[r + 1].v[2]] == host_off[w.ops[r].v[2]] + (int64_t)w.stride)
+        ++r;
+      uint64_t waited = 0;  // events this run already waits on (a batch releases many slots)
+      static_assert(kEvents <= 64, "one bit per event");
+      for (size_t q = k; q <= r; ++q) {
+        const int32_t* u = w.ops[q].v;
+        // a reader batch that has already finished needs no stream wait
+        if (u[4] >= 0 && !((waited >> u[4]) & 1) && hipEventQuery(w.used[u[4]]) != hipSuccess) {
+          if (!ok(hipStreamWaitEvent(w.copy, w.used[u[4]], 0))) return MOE_EHIP;
+          waited |= uint64_t{1} << u[4];
+          ++w.stats[kStCopyWaits];
+        }
+        w.slot_of[u[1]] = u[3];
+        ++w.stats[kStCopies];
+        w.stats[kStBytes] += (int64_t)eb;
       }
-      if (!ok(hipMemcpyAsync(w.ring + (size_t)v[3] * w.stride, arena + host_off[v[2]], eb,
+      const size_t bytes = (r - k) * w.stride + eb;
+      if (!ok(hipMemcpyAsync(w.ring + (size_t)v[3] * w.stride, arena + host_off[v[2]], bytes,
                              hipMemcpyHostToDevice, w.copy)))
         return MOE_EHIP;
-      w.slot_of[v[1]] = v[3];
-      ++w.stats[kStCopies];
-      w.stats[kStBytes] += (int64_t)eb;
+      ++w.stats[kStTransfers];
+      k = r;
     } else if (v[0] == kOpGather) {
       if (v[3]) {
         if (!ok(hipEventRecord(w.copied, w.copy)) || !ok(hipStreamWaitEvent(s, w.copied, 0)))
