@@ -81,16 +81,19 @@ __global__ __launch_bounds__(kGatherThreads) void gather_all_kernel(
 //   Q8_0, G = 136: d of the 4 blocks, then their q[32]
 // The expert keeps its order (gate | up | down) and its size.  A 64-row tile is one contiguous
 // run in the raw expert and one in the packed expert, so a workgroup moves a tile's rows for
-// up to kPackStages stages: it reads the rows' bytes into LDS with wide coalesced loads and
-// writes the tile-stages out, also coalesced, picking each output word from LDS.  Both the
-// pool reads and the packed writes are non-temporal: each byte is moved once.
+// up to Pack<WT>::kStages stages: it reads the rows' bytes into LDS with wide coalesced loads
+// and writes the tile-stages out, also coalesced, picking each output word from LDS.  Both the
+// pool reads and the packed writes are non-temporal: each byte is moved once.  Q4_1 items span
+// 8 stages (640 bytes of a row: whole 128-byte lines, so no line is fetched by two items);
+// Q8_0 items span 4 (544 bytes; 8 would leave too few workgroups per CU).
 
-constexpr int kPackStages = 4;
+constexpr int kLoadBatch = 8;  // loads a lane has in flight when it fills the LDS
 
 template <int WT>
 struct Pack {
   static constexpr int kG = WT == 1 ? 80 : 136;
-  static constexpr int kLds = 64 * kPackStages * kG;
+  static constexpr int kStages = WT == 1 ? 8 : 4;
+  static constexpr int kLds = 64 * kStages * kG;
 };
 
 // Byte offset, within a row's 4-block group in the raw layout, of the low half of output word k
@@ -119,7 +122,8 @@ __device__ __forceinline__ void pack_item(const uint8_t* __restrict__ src_e,
                                           uint8_t* lds) {
   constexpr int G = Pack<WT>::kG;
   const int sh = H / 128, sf = F / 128;
-  const int cg = (sh + kPackStages - 1) / kPackStages, cd = (sf + kPackStages - 1) / kPackStages;
+  constexpr int kPS = Pack<WT>::kStages;
+  const int cg = (sh + kPS - 1) / kPS, cd = (sf + kPS - 1) / kPS;
   const int items_gu = (F / 64) * cg;
   int tile, chunk, nS;
   size_t mat_off;
@@ -133,26 +137,48 @@ __device__ __forceinline__ void pack_item(const uint8_t* __restrict__ src_e,
     mat_off = (size_t)2 * F * sh * G;
   }
   const size_t row_bytes = (size_t)nS * G;
-  const int t0 = chunk * kPackStages, ns = min(kPackStages, nS - t0);
+  const int t0 = chunk * kPS, ns = min(kPS, nS - t0);
   const int seg = ns * G;  // bytes of one row in this item
   const uint8_t* s = src_e + mat_off + (size_t)tile * 64 * row_bytes + (size_t)t0 * G;
   uint8_t* d = dst_e + mat_off + ((size_t)tile * nS + t0) * 64 * G;
   const int tid = threadIdx.x;
 
-  // rows -> LDS (row i at i * seg), in the widest pieces the alignment allows
+  // rows -> LDS (row i at i * seg), in the widest pieces the alignment allows; each lane issues
+  // up to kLoadBatch loads before it waits for the first, so that enough bytes are in flight
+  // per CU to cover the HBM latency
   if (((uintptr_t)s & 15) == 0 && (row_bytes & 15) == 0 && (seg & 15) == 0) {
     const int per_row = seg / 16, total = 64 * per_row;
-    for (int q = tid; q < total; q += kGatherThreads) {
-      const int i = q / per_row, k = q % per_row;
-      *reinterpret_cast<v4u*>(lds + 16 * q) =
-          __builtin_nontemporal_load(reinterpret_cast<const v4u*>(s + i * row_bytes + 16 * k));
+    for (int q0 = tid; q0 < total; q0 += kLoadBatch * kGatherThreads) {
+      v4u r[kLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int q = q0 + u * kGatherThreads;
+        if (q < total)
+          r[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4u*>(s + (q / per_row) * row_bytes + 16 * (q % per_row)));
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int q = q0 + u * kGatherThreads;
+        if (q < total) *reinterpret_cast<v4u*>(lds + 16 * q) = r[u];
+      }
     }
   } else if (((uintptr_t)s & 7) == 0 && (row_bytes & 7) == 0) {
     const int per_row = seg / 8, total = 64 * per_row;
-    for (int q = tid; q < total; q += kGatherThreads) {
-      const int i = q / per_row, k = q % per_row;
-      *reinterpret_cast<v2u*>(lds + 8 * q) =
-          __builtin_nontemporal_load(reinterpret_cast<const v2u*>(s + i * row_bytes + 8 * k));
+    for (int q0 = tid; q0 < total; q0 += kLoadBatch * kGatherThreads) {
+      v2u r[kLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int q = q0 + u * kGatherThreads;
+        if (q < total)
+          r[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const v2u*>(s + (q / per_row) * row_bytes + 8 * (q % per_row)));
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int q = q0 + u * kGatherThreads;
+        if (q < total) *reinterpret_cast<v2u*>(lds + 8 * q) = r[u];
+      }
     }
   } else {
     for (int q = tid; q < 64 * seg; q += kGatherThreads) {
@@ -187,10 +213,10 @@ __device__ __forceinline__ void pack_item(const uint8_t* __restrict__ src_e,
   __syncthreads();  // the LDS is reused by the next item of this workgroup
 }
 
-int pack_items(int H, int F) {
+int pack_items(int wtype, int H, int F) {
   const int sh = H / 128, sf = F / 128;
-  return 2 * (F / 64) * ((sh + kPackStages - 1) / kPackStages) +
-         (H / 64) * ((sf + kPackStages - 1) / kPackStages);
+  const int ps = wtype == 1 ? Pack<1>::kStages : Pack<0>::kStages;
+  return 2 * (F / 64) * ((sh + ps - 1) / ps) + (H / 64) * ((sf + ps - 1) / ps);
 }
 
 template <int WT>
@@ -254,7 +280,7 @@ hipError_t launch_gather_all(const uint8_t* pool, const int64_t* expert_off, con
 hipError_t launch_gather_group_mmq(const GatherPtrs& p, int n, int wtype, int H, int F,
                                    uint8_t* dst, int first_pos, size_t pos_stride,
                                    hipStream_t s) {
-  const dim3 grid(pack_items(H, F), n);
+  const dim3 grid(pack_items(wtype, H, F), n);
   if (wtype == 1)
     gather_mmq_group_kernel<1><<<grid, kGatherThreads, 0, s>>>(p, H, F, dst, first_pos, pos_stride);
   else
@@ -267,7 +293,7 @@ hipError_t launch_gather_all_mmq(const uint8_t* pool, const int64_t* expert_off,
                                  int group_size, int wtype, int H, int F, uint8_t* dst,
                                  size_t stride, hipStream_t s) {
   const int groups = (max_slots + group_size - 1) / group_size;
-  const dim3 grid(pack_items(H, F), group_size, groups);
+  const dim3 grid(pack_items(wtype, H, F), group_size, groups);
   if (wtype == 1)
     gather_mmq_all_kernel<1><<<grid, kGatherThreads, 0, s>>>(pool, expert_off, order, n_active, H,
                                                              F, dst, stride);
