@@ -227,6 +227,44 @@ def streamed_walk(args, c, layer, x, logits, out, dev):
     print(json.dumps(line))
 
 
+def packed_layer(args, c, layer, x, logits, out, dev):
+    """Steps of routing + moe_prefill_layer_packed (no gather); prints one JSON line."""
+    import torch
+    layer.pack_pool()
+
+    def step():
+        idx, w = layer.route(logits)
+        layer.forward_packed(x, idx, w, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    line = {
+        "metric": "routed rows/sec (TxK) for the MoE prefill layer, packed resident experts "
+                  "(no gather)",
+        "value": round(c.T * c.K * args.steps / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}", "walk": "packed"},
+        "roofline": None,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,11 +277,12 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the steps (counter "
                          "calibration; outside the timed region)")
-    ap.add_argument("--walk", choices=["resident", "streamed"], default="resident",
+    ap.add_argument("--walk", choices=["resident", "streamed", "packed"], default="resident",
                     help="resident: every expert in HBM, the layer's one-launch schedule; "
                          "streamed: moe_prefill_layer_streamed, experts copied from a pinned "
-                         "host arena through a ring of device slots (another line, not the "
-                         "headline)")
+                         "host arena through a ring of device slots; packed: "
+                         "moe_prefill_layer_packed, experts kept in the MMQ layout and read in "
+                         "place, no gather (the last two print other lines, not the headline)")
     ap.add_argument("--ring-slots", type=int, default=96)
     ap.add_argument("--resident-frac", type=float, default=0.0,
                     help="streamed walk: the fraction of experts held in HBM (not copied)")
@@ -275,6 +314,9 @@ def main():
 
     if args.walk == "streamed":
         streamed_walk(args, c, layer, x, logits, out, dev)
+        return
+    if args.walk == "packed":
+        packed_layer(args, c, layer, x, logits, out, dev)
         return
 
     for _ in range(args.warmup):

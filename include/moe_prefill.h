@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_GROUP 16     /* experts per group buffer ([G1] "What": MMQ_GROUP = 16) */
 #define MOE_MAX_E 2048       /* largest expert count the kernels accept */
 #define MOE_MAX_K 64         /* largest routes per token */
@@ -166,6 +166,20 @@ int moe_prefill_layer(const float *x, int T, int H, int F, int E, int K,
                       const void *pool, const int64_t *expert_off, size_t expert_bytes,
                       int group_size, int ring_start, void *ws, size_t ws_bytes, float *out,
                       void *stream);
+
+/* a1, a2, a4..a7  The layer over experts that stay resident in the MMQ layout, with no gather
+ * (the pages' gather exists to assemble a group buffer from expert slots, [G1] "What"; an expert
+ * pool that never leaves device memory can be put in the matmul's layout once, with
+ * moe_gather_group_mmq, and read in place).  packed_pool: expert e in the MMQ layout at byte
+ * expert_off[e] (int64 [E], device; multiples of 16: a tile whose weights are not 16-byte
+ * aligned is skipped and its rows are unspecified).  The products, their order and so the
+ * output are those of moe_prefill_layer with the same arguments, bit for bit; ws as there
+ * (moe_workspace_size with any group size; the group region is not used). */
+int moe_prefill_layer_packed(const float *x, int T, int H, int F, int E, int K,
+                             const int32_t *topk_idx, const float *topk_w, int wtype,
+                             const void *packed_pool, const int64_t *expert_off,
+                             size_t expert_bytes, int ring_start, void *ws, size_t ws_bytes,
+                             float *out, void *stream);
 
 /* Where moe_prefill_layer keeps its intermediate results inside ws, for checking them:
  * the byte offset of region `which` (MOE_WS_*) for these arguments, or (size_t)-1. */

@@ -50,6 +50,7 @@ SIGNATURES = {
     "moe_mmq_grouped": (I, [I, P, SZ, SZ, I, I, P, I, P, I, P, I, P, P, P]),
     "moe_combine": (I, [P, P, P, I, I, I, P, P]),
     "moe_prefill_layer": (I, [P, I, I, I, I, I, P, P, I, P, P, SZ, I, I, P, SZ, P, P]),
+    "moe_prefill_layer_packed": (I, [P, I, I, I, I, I, P, P, I, P, P, SZ, I, P, SZ, P, P]),
     "moe_workspace_offset": (SZ, [I, I, I, I, I, I, I, I]),
     "moe_walk_create": (I, [P, I, SZ, P]),
     "moe_walk_destroy": (I, [P]),
@@ -221,6 +222,21 @@ def raw_prefill_layer(x, topk_idx, topk_w, wtype, pool, expert_off, F, E, group_
 
 def prefill_layer(*args, **kw):
     _check("moe_prefill_layer", raw_prefill_layer(*args, **kw))
+
+
+def raw_prefill_layer_packed(x, topk_idx, topk_w, wtype, packed_pool, expert_off, F, E,
+                             ring_start, ws, out, stream=None):
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    eb = expert_bytes(H, F, wtype)
+    return lib().moe_prefill_layer_packed(_ptr(x), T, H, F, E, K, _ptr(topk_idx), _ptr(topk_w),
+                                          wtype, _ptr(packed_pool), _ptr(expert_off), eb,
+                                          ring_start, _ptr(ws), ws.numel() * ws.element_size(),
+                                          _ptr(out), _stream(stream))
+
+
+def prefill_layer_packed(*args, **kw):
+    _check("moe_prefill_layer_packed", raw_prefill_layer_packed(*args, **kw))
 
 
 def profile_begin(n_calls: int) -> None:

@@ -261,6 +261,54 @@ int moe_prefill_layer(const float* x, int T, int H, int F, int E, int K, const i
   return MOE_OK;
 }
 
+int moe_prefill_layer_packed(const float* x, int T, int H, int F, int E, int K,
+                             const int32_t* topk_idx, const float* topk_w, int wtype,
+                             const void* packed_pool, const int64_t* expert_off,
+                             size_t expert_bytes, int ring_start, void* ws, size_t ws_bytes,
+                             float* out, void* stream) {
+  if (!packed_pool || !expert_off) return MOE_EINVAL;
+  Layout L;
+  const int rc = check_layer_args(x, T, H, F, E, K, topk_idx, topk_w, wtype, expert_bytes,
+                                  MOE_MAX_GROUP, ring_start, ws, ws_bytes, out, &L);
+  if (rc != MOE_OK) return rc;
+  if (!aligned(packed_pool, 16)) return MOE_EINVAL;
+
+  hipStream_t s = as_stream(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  MapsOut mo{I32(L.counts), I32(L.offsets), I32(L.src), I32(L.slot), I32(L.order),
+             I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
+             I32(L.ntiles), kMmqRows};
+  if (launch_build_maps(topk_idx, T, K, E, ring_start, mo, s) != hipSuccess ||
+      launch_quantize(x, T, H, K, mo.slot, mo.src, 0, base + L.q8x, s) != hipSuccess)
+    return MOE_EHIP;
+  MmqProblem gu{};
+  gu.wtype = wtype;
+  gu.epilogue = MOE_EPI_SWIGLU_Q8_1;
+  gu.wbase = static_cast<const uint8_t*>(packed_pool);
+  gu.w_off = expert_off;
+  gu.mat_offset = 0;
+  gu.n_out = F;
+  gu.k_in = H;
+  gu.act = base + L.q8x;
+  gu.out = base + L.hq8;
+  gu.tiles = mo.tiles;
+  gu.n_tiles = mo.n_tiles;
+  gu.max_tiles = L.max_tiles;
+  MmqProblem dn = gu;
+  dn.epilogue = MOE_EPI_F32;
+  dn.mat_offset = (size_t)2 * F * (H / 32) * moe_block_bytes(wtype);
+  dn.n_out = H;
+  dn.k_in = F;
+  dn.act = base + L.hq8;
+  dn.out = base + L.dm;
+  if (launch_mmq(gu, s) != hipSuccess || launch_mmq(dn, s) != hipSuccess ||
+      launch_combine(reinterpret_cast<const float*>(base + L.dm), mo.slot, topk_w, T, K, H, out,
+                     s) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
 int moe_profile_begin(int n_calls) {
   if (n_calls < 1 || n_calls > 100000) return MOE_EINVAL;
   std::lock_guard<std::mutex> lk(g_prof_mu);

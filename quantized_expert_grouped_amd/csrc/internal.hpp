@@ -72,8 +72,9 @@ constexpr int kMmqRows = 64;  // rows per m-tile
 struct MmqProblem {
   int wtype;
   int epilogue;           // 0 f32, 1 swiglu->q8_1, 2 int32 block dots
-  const uint8_t* wbase;   // group buffer(s)
+  const uint8_t* wbase;   // group buffer(s), or the packed pool when w_off is set
   size_t pos_stride;      // bytes between expert positions
+  const int64_t* w_off;   // if set: expert e's MMQ-layout bytes at wbase + w_off[e]
   size_t mat_offset;      // bytes from an expert's start to the matrix
   int n_out;
   int k_in;

@@ -439,7 +439,10 @@ __global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
 #endif
   const int mt = work / ntl;
   const MTile t = p.tiles[mt];
-  const uint8_t* W = p.wbase + (size_t)t.ordinal * p.pos_stride + p.mat_offset;
+  const uint8_t* W = p.mat_offset + (p.w_off != nullptr
+                                         ? p.wbase + p.w_off[t.expert]
+                                         : p.wbase + (size_t)t.ordinal * p.pos_stride);
+  if (((uintptr_t)W & 15) != 0) return;  // the direct-to-LDS loads need 16-byte alignment
   mmq_tile<WT, EPI>(L0, L1, L2, p, W, t.row0, t.nrows, work % ntl);
 }
 

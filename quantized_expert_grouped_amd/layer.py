@@ -47,6 +47,31 @@ class MoePrefillLayer:
                           rs, self.ws, out)
         return out
 
+    def pack_pool(self) -> torch.Tensor:
+        """The pool with every expert put in the MMQ layout at its own offset (one gather launch
+        per expert; done once, the experts never change), for forward_packed."""
+        packed = torch.zeros_like(self.pool)
+        off = self.expert_off.cpu().numpy()
+        base, dst = self.pool.data_ptr(), packed.data_ptr()
+        for e in range(self.E):
+            o = int(off[e])
+            abi.gather_group_mmq([base + o], self.wtype, self.H, self.F, dst + o, 0, 0)
+        self.packed = packed
+        return packed
+
+    def forward_packed(self, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                       out: torch.Tensor | None = None, ring_start: int | None = None):
+        """The layer reading the packed pool in place (no gather); pack_pool() first."""
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"T={T} exceeds the workspace's {self.max_tokens} tokens")
+        if out is None:
+            out = torch.empty((T, self.H), dtype=torch.float32, device=self.device)
+        rs = self.ring_start if ring_start is None else ring_start
+        abi.prefill_layer_packed(x, idx, w, self.wtype, self.packed, self.expert_off, self.F,
+                                 self.E, rs, self.ws, out)
+        return out
+
     def step(self, x: torch.Tensor, logits: torch.Tensor, out: torch.Tensor | None = None):
         """One pass of the whole hot path: routing, then the layer."""
         idx, w = self.route(logits)

@@ -142,3 +142,25 @@ def test_layer_repeat_is_deterministic(orc):
     a = _run(layer, c, idx, w)
     b = _run(layer, c, idx, w)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[4]], ids=["tiny", "ragged_q4_1", "skew"])
+def test_layer_packed_pool_equals_gathered_layer(orc, case):
+    """Experts kept in the MMQ layout and read in place (no gather): the same bytes reach the
+    matmul, so the output is the gathered layer's bit for bit."""
+    name, T, H, F, E, K, wtype, zipf = case
+    c = synth.make_case(name, T=T, H=H, F=F, E=E, K=K, wtype=wtype,
+                        seed=zlib.crc32(name.encode()) % 10000, zero_tokens=(T // 3,), zipf=zipf)
+    idx, w = orc.route_topk(c.logits, K)
+    layer = _layer(c)
+    ref = _run(layer, c, idx, w)
+    packed = layer.pack_pool()
+    # the packed pool is the oracle's MMQ layout of every expert
+    ph = host(packed)
+    for e in range(E):
+        o = int(c.expert_off[e])
+        assert np.array_equal(ph[o:o + c.expert_bytes], orc.mmq_pack(wtype, c.expert(e), H, F)), e
+    note(f"packed layer {name}")
+    for rs in (c.ring_start, 0):
+        got = host(layer.forward_packed(dev(c.x), dev(idx), dev(w), ring_start=rs))
+        assert np.array_equal(got, ref), rs
