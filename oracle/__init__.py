@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q8_0, Q4_1 = 0, 1
+Q8_0, Q4_1, Q8_0_D4 = 0, 1, 2      # Q8_0_D4: Q8_0 weights, D4 activations
+DS4, D4 = 0, 1
 
 _lib = None
 
@@ -55,8 +56,9 @@ def lib():
             "orc_build_maps": (None, [P, i, i, i, i, P, P, P, P, P, P]),
             "orc_q8_1_block": (None, [P, P, P, P]),
             "orc_q8_1_row": (None, [P, i, P]),
-            "orc_quantize_gather": (None, [P, i, i, i, P, P]),
-            "orc_quantize_scatter": (None, [P, i, i, i, P, P]),
+            "orc_q8_1_row_d4": (None, [P, i, P]),
+            "orc_quantize_gather": (None, [P, i, i, i, P, i, P]),
+            "orc_quantize_scatter": (None, [P, i, i, i, P, i, P]),
             "orc_gather": (None, [P, P, P, i, sz, P, i, sz]),
             "orc_mmq_expert_bytes": (sz, [i, i, i]),
             "orc_mmq_pack": (None, [i, P, i, i, P]),
@@ -154,33 +156,39 @@ def q8_1_block(v):
     return q, int(d[0]), int(s[0])
 
 
-def q8_1_rows(v):
-    """Quantise every row of a [N x n] fp32 array to DS4 q8_1 bytes [N x n/128*144]."""
+def q8_1_rows(v, layout: int = DS4):
+    """Quantise every row of a [N x n] fp32 array to q8_1 bytes [N x n/128*144] (DS4 or D4)."""
     v = _c(v, np.float32)
     N, n = v.shape
     rb = q8_1_row_bytes(n)
     out = np.empty((N, rb), np.uint8)
     L = lib()
+    fn = L.orc_q8_1_row_d4 if layout == D4 else L.orc_q8_1_row
     for r in range(N):
-        L.orc_q8_1_row(_p(v[r]), n, _p(out[r]))
+        fn(_p(v[r]), n, _p(out[r]))
     return out
 
 
-def quantize_gather(x, K: int, src):
+def act_layout(wtype: int) -> int:
+    """The q8_1 layout of a weight type's activations."""
+    return D4 if wtype == Q8_0_D4 else DS4
+
+
+def quantize_gather(x, K: int, src, layout: int = DS4):
     x = _c(x, np.float32)
     src = _c(src, np.int32)
     T, H = x.shape
     out = np.empty((T * K, q8_1_row_bytes(H)), np.uint8)
-    lib().orc_quantize_gather(_p(x), T, H, K, _p(src), _p(out))
+    lib().orc_quantize_gather(_p(x), T, H, K, _p(src), layout, _p(out))
     return out
 
 
-def quantize_scatter(x, K: int, slot):
+def quantize_scatter(x, K: int, slot, layout: int = DS4):
     x = _c(x, np.float32)
     slot = _c(slot, np.int32)
     T, H = x.shape
     out = np.empty((T * K, q8_1_row_bytes(H)), np.uint8)
-    lib().orc_quantize_scatter(_p(x), T, H, K, _p(slot), _p(out))
+    lib().orc_quantize_scatter(_p(x), T, H, K, _p(slot), layout, _p(out))
     return out
 
 

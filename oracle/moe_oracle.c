@@ -56,7 +56,7 @@ double orc_f16_to_f64(uint16_t h)
 static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 static void wr16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)(v & 0xff); p[1] = (uint8_t)(v >> 8); }
 
-size_t orc_block_bytes(int wtype) { return wtype == ORC_Q8_0 ? 34 : 20; }
+size_t orc_block_bytes(int wtype) { return wtype == ORC_Q4_1 ? 20 : 34; }
 
 size_t orc_expert_bytes(int H, int F, int wtype)
 {
@@ -207,28 +207,62 @@ void orc_q8_1_row(const float *v, int n, uint8_t *out)
     }
 }
 
+/* The D4 layout.  [QS] "Identity" names D4 as the q8_1 layout the MMQ uses for Q8_0 (and
+ * Q2_0, IQ2_XS) beside DS4 for Q4_1, and gives nothing but the name.  Reading: "D4" = four d
+ * per 128-value group, kept in fp32 (the scale before it is rounded to fp16), no s (only Q4_1's
+ * min term needs one): per 128 values a 144-byte group of 4 x fp32 d, then the 4 blocks' q.
+ * The q are those of the DS4 form (the same fp32 d divides the values).
+ * Pinned in tests/test_oracle_q8_1.py. */
+void orc_q8_1_row_d4(const float *v, int n, uint8_t *out)
+{
+    for (int g = 0; g < n / 128; ++g) {
+        uint8_t *grp = out + (size_t)g * 144;
+        for (int j = 0; j < 4; ++j) {
+            const float *b = v + (size_t)g * 128 + 32 * j;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(b[i]) > amax) amax = fabsf(b[i]);
+            float d = amax / 127.0f;
+            int8_t q[32];
+            for (int i = 0; i < 32; ++i) q[i] = amax == 0.0f ? 0 : (int8_t)(int)roundf(b[i] / d);
+            memcpy(grp + 4 * j, &d, 4);
+            memcpy(grp + 16 + 32 * j, q, 32);
+        }
+    }
+}
+
+static void q8_1_row_layout(int layout, const float *v, int n, uint8_t *out)
+{
+    if (layout == ORC_D4)
+        orc_q8_1_row_d4(v, n, out);
+    else
+        orc_q8_1_row(v, n, out);
+}
+
 /* [QS] opening section: the per-row ("gather") form quantises the T x K rows in expert
  * order, reading token src[r]/K's input row once for every row r. */
-void orc_quantize_gather(const float *x, int T, int H, int K, const int32_t *src, uint8_t *q8)
+void orc_quantize_gather(const float *x, int T, int H, int K, const int32_t *src, int layout,
+                         uint8_t *q8)
 {
     size_t rb = orc_q8_1_row_bytes(H);
     int R = T * K;
 #pragma omp parallel for schedule(static)
     for (int r = 0; r < R; ++r) {
         int t = src[r] / K;
-        orc_q8_1_row(x + (size_t)t * H, H, q8 + (size_t)r * rb);
+        q8_1_row_layout(layout, x + (size_t)t * H, H, q8 + (size_t)r * rb);
     }
 }
 
 /* [QS] opening section: the scatter form quantises each token once and writes the same
  * bytes to each of its K rows slot[t*K+k]. */
-void orc_quantize_scatter(const float *x, int T, int H, int K, const int32_t *slot, uint8_t *q8)
+void orc_quantize_scatter(const float *x, int T, int H, int K, const int32_t *slot, int layout,
+                          uint8_t *q8)
 {
     size_t rb = orc_q8_1_row_bytes(H);
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         uint8_t *row = q8 + (size_t)slot[(size_t)t * K] * rb;
-        orc_q8_1_row(x + (size_t)t * H, H, row);
+        q8_1_row_layout(layout, x + (size_t)t * H, H, row);
         for (int k = 1; k < K; ++k)
             memcpy(q8 + (size_t)slot[(size_t)t * K + k] * rb, row, rb);
     }
@@ -309,17 +343,18 @@ void orc_gather_mmq(const uint8_t *pool, const int64_t *expert_off, const int32_
  * a4 / a6  block dots (MMQ).  [G2] "What changes" and [QS] opening section: the grouped
  * quantised matmul on q8_1 activations.  For weight block b of row n and activation block b
  * of row r:  I_b = sum_j qw_j * qx_j  (integer),
- *   Q8_0:  y_b = dw * dx * I_b
+ *   Q8_0:  y_b = dw * dx * I_b                (dx: fp16 d of DS4, or fp32 d of D4)
  *   Q4_1:  y_b = dw * dx * I_b + mw * sx      (w_j = dw*qw_j + mw, and sx = d*sum qx is what
  *                                             the DS4 layout stores for exactly this term)
- * and the row result is sum_b y_b over b ascending, in fp64 (fp16 -> fp64 is exact and
- * dw*dx*I_b has at most 41 significant bits, so every y_b is exact).
+ * and the row result is sum_b y_b over b ascending, in fp64 (fp16 -> fp64 is exact and, with
+ * DS4, dw*dx*I_b has at most 41 significant bits, so every y_b is exact; with D4's fp32 dx it
+ * has up to 55 and dw*dx*I_b is rounded once, to 2^-53 relative).
  * Pinned in tests/test_oracle_gather_dot.py against an fp64 dequantised brute force.
  * ------------------------------------------------------------------------------------- */
 int32_t orc_block_idot(int wtype, const uint8_t *wblock, const int8_t *xq)
 {
     int32_t I = 0;
-    if (wtype == ORC_Q8_0) {
+    if (wtype != ORC_Q4_1) {
         const int8_t *qw = (const int8_t *)(wblock + 2);
         for (int j = 0; j < 32; ++j) I += (int32_t)qw[j] * (int32_t)xq[j];
     } else {
@@ -338,8 +373,15 @@ double orc_row_dot(int wtype, const uint8_t *wrow, const uint8_t *xrow_q8, int k
     double acc = 0.0;
     for (int b = 0; b < k_in / 32; ++b) {
         const uint8_t *grp = xrow_q8 + (size_t)(b / 4) * 144;
-        double dx = orc_f16_to_f64(rd16(grp + 4 * (b % 4)));
-        double sx = orc_f16_to_f64(rd16(grp + 4 * (b % 4) + 2));
+        double dx, sx = 0.0;
+        if (wtype == ORC_Q8_0_D4) {  /* fp32 d, no s */
+            float d32;
+            memcpy(&d32, grp + 4 * (b % 4), 4);
+            dx = (double)d32;
+        } else {
+            dx = orc_f16_to_f64(rd16(grp + 4 * (b % 4)));
+            sx = orc_f16_to_f64(rd16(grp + 4 * (b % 4) + 2));
+        }
         const int8_t *xq = (const int8_t *)(grp + 16 + 32 * (b % 4));
         const uint8_t *blk = wrow + (size_t)b * bb;
         double dw = orc_f16_to_f64(rd16(blk));
@@ -403,7 +445,7 @@ void orc_expert_row(int wtype, const uint8_t *expert, int H, int F, const uint8_
         double u = orc_row_dot(wtype, up + (size_t)f * gu_row, xrow_q8, H);
         h[f] = (float)(g / (1.0 + exp(-g)) * u);
     }
-    orc_q8_1_row(h, F, hq8);
+    q8_1_row_layout(wtype == ORC_Q8_0_D4 ? ORC_D4 : ORC_DS4, h, F, hq8);
     for (int i = 0; i < H; ++i) dm[i] = orc_row_dot(wtype, down + (size_t)i * dn_row, hq8, F);
 }
 
@@ -448,7 +490,7 @@ int orc_prefill_layer(const float *x, int T, int H, int F, int E, int K,
 
     uint8_t *q8 = q8x ? q8x : (uint8_t *)malloc(xrb * (size_t)R);
     double *dm = Dm ? Dm : (double *)malloc(sizeof(double) * (size_t)R * H);
-    orc_quantize_scatter(x, T, H, K, slot, q8);
+    orc_quantize_scatter(x, T, H, K, slot, wtype == ORC_Q8_0_D4 ? ORC_D4 : ORC_DS4, q8);
 
 #pragma omp parallel
     {
@@ -485,7 +527,7 @@ void orc_token_out(const float *x_row, int H, int F, int K, const int32_t *idx_r
     float *hrow = (float *)malloc(sizeof(float) * (size_t)F);
     uint8_t *hq = (uint8_t *)malloc(orc_q8_1_row_bytes(F));
     double *dm = (double *)malloc(sizeof(double) * (size_t)K * H);
-    orc_q8_1_row(x_row, H, xq);
+    q8_1_row_layout(wtype == ORC_Q8_0_D4 ? ORC_D4 : ORC_DS4, x_row, H, xq);
     for (int k = 0; k < K; ++k)
         orc_expert_row(wtype, pool + expert_off[idx_row[k]], H, F, xq, hrow, hq,
                        dm + (size_t)k * H);

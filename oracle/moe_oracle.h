@@ -40,7 +40,12 @@
 extern "C" {
 #endif
 
-enum { ORC_Q8_0 = 0, ORC_Q4_1 = 1 };
+/* Weight type, and with it the activations' q8_1 layout:
+ *   ORC_Q8_0    Q8_0 weights, DS4 activations (4 x (fp16 d, fp16 s) per 128 values)
+ *   ORC_Q4_1    Q4_1 weights, DS4 activations
+ *   ORC_Q8_0_D4 Q8_0 weights, D4 activations (4 x fp32 d per 128 values, no s) */
+enum { ORC_Q8_0 = 0, ORC_Q4_1 = 1, ORC_Q8_0_D4 = 2 };
+enum { ORC_DS4 = 0, ORC_D4 = 1 };
 
 /* --- number formats ------------------------------------------------------------------- */
 uint16_t orc_f32_to_f16(float f);      /* IEEE binary16, round to nearest even, subnormals kept */
@@ -64,8 +69,11 @@ void orc_build_maps(const int32_t *idx, int T, int K, int E, int ring_start,
 /* --- a2 / a5 q8_1 ------------------------------------------------------------------------ */
 void orc_q8_1_block(const float *v, int8_t *q, uint16_t *d16, uint16_t *s16);
 void orc_q8_1_row(const float *v, int n, uint8_t *out);
-void orc_quantize_gather(const float *x, int T, int H, int K, const int32_t *src, uint8_t *q8);
-void orc_quantize_scatter(const float *x, int T, int H, int K, const int32_t *slot, uint8_t *q8);
+void orc_q8_1_row_d4(const float *v, int n, uint8_t *out);
+void orc_quantize_gather(const float *x, int T, int H, int K, const int32_t *src, int layout,
+                         uint8_t *q8);
+void orc_quantize_scatter(const float *x, int T, int H, int K, const int32_t *slot, int layout,
+                          uint8_t *q8);
 
 /* --- a3 gather ------------------------------------------------------------------------- */
 void orc_gather(const uint8_t *pool, const int64_t *expert_off, const int32_t *experts, int n,

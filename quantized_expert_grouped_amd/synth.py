@@ -28,9 +28,9 @@ import dataclasses
 
 import numpy as np
 
-Q8_0, Q4_1 = 0, 1
-BLOCK_BYTES = {Q8_0: 34, Q4_1: 20}
-WTYPE_NAME = {Q8_0: "q8_0", Q4_1: "q4_1"}
+Q8_0, Q4_1, Q8_0_D4 = 0, 1, 2   # Q8_0_D4: Q8_0 weights, activations in the D4 q8_1 layout
+BLOCK_BYTES = {Q8_0: 34, Q4_1: 20, Q8_0_D4: 34}
+WTYPE_NAME = {Q8_0: "q8_0", Q4_1: "q4_1", Q8_0_D4: "q8_0_d4"}
 
 CONFIGS = {
     "tiny": dict(no=1, T=7, H=256, F=128, E=16, K=2, wtype=Q8_0, zero_tokens=(3,)),
@@ -102,7 +102,7 @@ def pack_q4_1(q: np.ndarray, d16: np.ndarray, m16: np.ndarray) -> np.ndarray:
 
 def random_blocks(rng: np.random.Generator, nb: int, wtype: int) -> np.ndarray:
     d16 = rng.uniform(1e-3, 1e-2, nb).astype(np.float16)
-    if wtype == Q8_0:
+    if wtype != Q4_1:  # Q8_0 blocks (Q8_0_D4 differs only in the activations' layout)
         q = rng.integers(-127, 128, size=(nb, 32), dtype=np.int8)
         return pack_q8_0(q, d16)
     q = rng.integers(0, 16, size=(nb, 32), dtype=np.uint8)

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import numpy as np
 
-Q8_0, Q4_1 = 0, 1
+Q8_0, Q4_1, Q8_0_D4 = 0, 1, 2    # Q8_0_D4: Q8_0 weights, D4 activations
 
 
 # ---- fp16 ------------------------------------------------------------------------------------
@@ -56,6 +56,36 @@ def q8_1_rows(v: np.ndarray) -> np.ndarray:
     return out.reshape(N, G * 144)
 
 
+def q8_1_rows_d4(v: np.ndarray) -> np.ndarray:
+    """[N, n] fp32 -> [N, n/128*144] bytes in the D4 layout: per 128 values the 4 blocks' fp32
+    d (amax/127, the value before any fp16 rounding), then their q (as in DS4)."""
+    v = np.asarray(v, np.float32)
+    N, n = v.shape
+    G = n // 128
+    blocks = v.reshape(N, G, 4, 32)
+    q, _, _ = q8_1_blocks(blocks)
+    d = (np.max(np.abs(blocks), axis=-1) / np.float32(127.0)).astype("<f4")   # 0 for zero blocks
+    out = np.empty((N, G, 144), np.uint8)
+    out[:, :, 0:16] = d.view(np.uint8).reshape(N, G, 16)
+    out[:, :, 16:] = q.view(np.uint8).reshape(N, G, 128)
+    return out.reshape(N, G * 144)
+
+
+def q8_1_rows_for(v: np.ndarray, wtype: int) -> np.ndarray:
+    return q8_1_rows_d4(v) if wtype == Q8_0_D4 else q8_1_rows(v)
+
+
+def q8_1_decode_d4(rows: np.ndarray, n: int):
+    """D4 bytes -> (q int [N, n], dx [N, n/32] fp64 of the fp32 d, sx zeros)."""
+    rows = np.asarray(rows, np.uint8)
+    N = rows.shape[0]
+    G = n // 128
+    g = rows.reshape(N, G, 144)
+    d = g[:, :, 0:16].copy().view("<f4").reshape(N, G * 4).astype(np.float64)
+    q = g[:, :, 16:].copy().view(np.int8).reshape(N, n).astype(np.int64)
+    return q, d, np.zeros_like(d)
+
+
 def q8_1_decode(rows: np.ndarray, n: int):
     """DS4 bytes -> (q int [N, n], dx [N, n/32], sx [N, n/32]) as fp64 values."""
     rows = np.asarray(rows, np.uint8)
@@ -73,10 +103,10 @@ def q8_1_decode(rows: np.ndarray, n: int):
 def unpack_matrix(raw: np.ndarray, n_rows: int, k_in: int, wtype: int):
     """Weight matrix bytes -> (q int [n_rows, k_in], d [n_rows, k_in/32], m or None)."""
     nb = k_in // 32
-    bb = 34 if wtype == Q8_0 else 20
+    bb = 20 if wtype == Q4_1 else 34
     blk = np.asarray(raw, np.uint8)[: n_rows * nb * bb].reshape(n_rows, nb, bb)
     d = f16_val(blk[:, :, 0:2].copy().view("<u2")[..., 0])
-    if wtype == Q8_0:
+    if wtype != Q4_1:
         q = blk[:, :, 2:34].copy().view(np.int8).astype(np.int64).reshape(n_rows, k_in)
         return q, d, None
     m = f16_val(blk[:, :, 2:4].copy().view("<u2")[..., 0])
@@ -102,7 +132,7 @@ def matrix_parts(raw, n_rows, k_in, wtype):
 
 def expert_mats(expert: np.ndarray, H: int, F: int, wtype: int):
     """(gate, up, down) as (A, M) pairs; gate is the first F rows, up the next F, then down."""
-    bb = 34 if wtype == Q8_0 else 20
+    bb = 20 if wtype == Q4_1 else 34
     gu = F * (H // 32) * bb
     gate = matrix_parts(expert[0:gu], F, H, wtype)
     up = matrix_parts(expert[gu:2 * gu], F, H, wtype)
@@ -110,17 +140,17 @@ def expert_mats(expert: np.ndarray, H: int, F: int, wtype: int):
     return gate, up, down
 
 
-def dequant_act(rows: np.ndarray, n: int) -> np.ndarray:
-    q, dx, _ = q8_1_decode(rows, n)
+def dequant_act(rows: np.ndarray, n: int, wtype: int = Q8_0) -> np.ndarray:
+    q, dx, _ = (q8_1_decode_d4 if wtype == Q8_0_D4 else q8_1_decode)(rows, n)
     N = q.shape[0]
     return (q.reshape(N, n // 32, 32) * dx[..., None]).reshape(N, n)
 
 
-def qproduct(parts, act_row: np.ndarray, n: int) -> np.ndarray:
+def qproduct(parts, act_row: np.ndarray, n: int, wtype: int = Q8_0) -> np.ndarray:
     """Weight matrix times one q8_1 activation row, in matrix form: A @ (dx*q) plus, for Q4_1,
     M @ s -- the min term uses the s the DS4 layout stores for it."""
     A, M = parts
-    q, dx, sx = q8_1_decode(act_row[None, :], n)
+    q, dx, sx = (q8_1_decode_d4 if wtype == Q8_0_D4 else q8_1_decode)(act_row[None, :], n)
     xh = (q.reshape(n // 32, 32) * dx[0][:, None]).reshape(n)
     y = A @ xh
     if M is not None:
@@ -165,7 +195,7 @@ def layer(x, idx, w, pool, expert_off, expert_bytes, H, F, wtype):
     x = np.asarray(x, np.float32)
     T = x.shape[0]
     K = idx.shape[1]
-    xq = q8_1_rows(x)
+    xq = q8_1_rows_for(x, wtype)
     out = np.zeros((T, H), np.float64)
     cache = {}
     for t in range(T):
@@ -175,10 +205,11 @@ def layer(x, idx, w, pool, expert_off, expert_bytes, H, F, wtype):
                 o = int(expert_off[e])
                 cache[e] = expert_mats(pool[o:o + expert_bytes], H, F, wtype)
             g_p, u_p, d_p = cache[e]
-            g = qproduct(g_p, xq[t], H)
-            u = qproduct(u_p, xq[t], H)
+            g = qproduct(g_p, xq[t], H, wtype)
+            u = qproduct(u_p, xq[t], H, wtype)
             h = (silu(g) * u).astype(np.float32)
-            out[t] += float(w[t, k]) * qproduct(d_p, q8_1_rows(h[None, :])[0], F)
+            out[t] += float(w[t, k]) * qproduct(d_p, q8_1_rows_for(h[None, :], wtype)[0], F,
+                                                wtype)
     return out
 
 
@@ -192,7 +223,7 @@ def layer_unquantized(x, idx, w, pool, expert_off, expert_bytes, H, F, wtype):
         for k in range(K):
             e = int(idx[t, k])
             o = int(expert_off[e])
-            bb = 34 if wtype == Q8_0 else 20
+            bb = 20 if wtype == Q4_1 else 34
             gu = F * (H // 32) * bb
             ex = pool[o:o + expert_bytes]
             g_m = dequant_matrix(ex[0:gu], F, H, wtype)

@@ -135,7 +135,7 @@ def test_block_idot_against_unpacked_integers(orc, wtype):
         assert orc.block_idot(wtype, b, np.full(32, 127, np.int8)) == -32 * 127 * 127
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 def test_row_dot_against_dequantised_fp64(orc, wtype):
     """sum_b y_b equals the fp64 dot of the dequantised weight row and activation row:
     exactly (to fp64 summation) for Q8_0; for Q4_1 up to the term m_w * (s16 - d16*sum q_x),
@@ -145,8 +145,8 @@ def test_row_dot_against_dequantised_fp64(orc, wtype):
     nb = k_in // 32
     x = rng.standard_normal((6, k_in)).astype(np.float32)
     x[2] = 0
-    xq8 = orc.q8_1_rows(x)
-    xh = npref.dequant_act(xq8, k_in)
+    xq8 = orc.q8_1_rows(x, orc.act_layout(wtype))
+    xh = npref.dequant_act(xq8, k_in, wtype)
     qx, dx, sx = npref.q8_1_decode(xq8, k_in)
     for _ in range(30):
         wrow = _block(wtype, rng, nb).reshape(-1)
@@ -178,15 +178,15 @@ def test_block_dots_matrix(orc, wtype):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 def test_mmq_rows_matrix_form(orc, wtype):
     """The products of many rows against numpy's matrix form (d*q dequantised, plus m @ s)."""
     rng = np.random.default_rng(18 + wtype)
     n_out, k_in = 9, 384
     wmat = _block(wtype, rng, n_out * k_in // 32).reshape(-1)
-    act = orc.q8_1_rows(rng.standard_normal((5, k_in)).astype(np.float32))
+    act = orc.q8_1_rows(rng.standard_normal((5, k_in)).astype(np.float32), orc.act_layout(wtype))
     got = orc.mmq_rows(wtype, wmat, n_out, k_in, act)
     parts = npref.matrix_parts(wmat, n_out, k_in, wtype)
     for r in range(5):
-        want = npref.qproduct(parts, act[r], k_in)
+        want = npref.qproduct(parts, act[r], k_in, wtype)
         assert np.allclose(got[r], want, rtol=1e-12, atol=1e-12)

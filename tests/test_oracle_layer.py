@@ -10,7 +10,7 @@ def _rel_err(a, b):
     return float(np.max(np.abs(np.asarray(a, np.float64) - b)) / max(np.max(np.abs(b)), 1e-300))
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 def test_dense_special_case(orc, wtype):
     """E = 1, K = 1, w = 1 reduces the layer to one quantised FFN, which numpy.matmul on the
     dequantised weights and activations computes independently (gate = first F rows)."""
@@ -24,8 +24,8 @@ def test_dense_special_case(orc, wtype):
     # K = 1, w = 1: the output is Dm rounded to fp32
     assert np.array_equal(out, dbg["Dm"].astype(np.float32))
     # the requantised h is the numpy quantiser's bytes of the oracle's own fp32 h
-    assert np.array_equal(dbg["hq8"], npref.q8_1_rows(dbg["h"]))
-    assert np.array_equal(dbg["q8x"], npref.q8_1_rows(c.x))
+    assert np.array_equal(dbg["hq8"], npref.q8_1_rows_for(dbg["h"], wtype))
+    assert np.array_equal(dbg["q8x"], npref.q8_1_rows_for(c.x, wtype))
 
 
 def test_swapped_gate_up_is_detected(orc):
@@ -42,7 +42,7 @@ def test_swapped_gate_up_is_detected(orc):
     assert _rel_err(out, ref_sw) > 1e-2
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 def test_tiny_layer_against_numpy(orc, wtype):
     """The five-config 'tiny' shape (T=7, H=256, F=128, E=16, K=2, token 3 zero) through
     the whole layer against the numpy dense chain per route."""
@@ -82,7 +82,7 @@ def test_combine_closed_forms(orc):
     assert np.array_equal(out, out2)
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 def test_token_out_equals_layer_rows(orc, wtype):
     c = synth.make_case(T=11, H=256, F=128, E=8, K=3, wtype=wtype, seed=31)
     idx, w = orc.route_topk(c.logits, c.K)
@@ -107,3 +107,20 @@ def test_layer_rejects_bad_shapes(orc):
     with pytest.raises(ValueError):
         orc.prefill_layer(c.x, idx, np.ones((2, 5), np.float32), c.wtype, c.pool, c.expert_off,
                           c.F, c.E)
+
+
+def test_d4_and_ds4_differ_only_by_the_activation_scales(orc):
+    """The same Q8_0 experts with D4 and with DS4 activations: the q bytes of x agree, the
+    outputs differ by about fp16's relative precision (DS4 rounds d to fp16, D4 keeps fp32)."""
+    a = synth.make_case(T=20, H=256, F=128, E=6, K=2, wtype=synth.Q8_0, seed=51)
+    b = synth.make_case(T=20, H=256, F=128, E=6, K=2, wtype=synth.Q8_0_D4, seed=51)
+    assert np.array_equal(a.pool, b.pool)
+    idx, w = orc.route_topk(a.logits, a.K)
+    oa, da = orc.prefill_layer(a.x, idx, w, a.wtype, a.pool, a.expert_off, a.F, a.E, debug=True)
+    ob, db = orc.prefill_layer(b.x, idx, w, b.wtype, b.pool, b.expert_off, b.F, b.E, debug=True)
+    G = a.H // 128
+    qa = da["q8x"].reshape(-1, G, 144)[:, :, 16:]
+    qb = db["q8x"].reshape(-1, G, 144)[:, :, 16:]
+    assert np.array_equal(qa, qb)
+    err = _rel_err(ob, oa.astype(np.float64))
+    assert 0 < err < 4e-3

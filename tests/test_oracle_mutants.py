@@ -54,6 +54,13 @@ MUTANTS = {
                            "uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 32) * G;"),
     "mmq_pack_row_major": ("uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;",
                            "uint8_t *dst = out + ((size_t)n * stages + t) * G;"),
+    "d4_header_fp16": ("memcpy(grp + 4 * j, &d, 4);",
+                       "{ float dr = (float)orc_f16_to_f64(orc_f32_to_f16(d)); memcpy(grp + 4 * j, &dr, 4); }"),
+    "d4_q_from_fp16_d": ("for (int i = 0; i < 32; ++i) q[i] = amax == 0.0f ? 0 : (int8_t)(int)roundf(b[i] / d);",
+                         "for (int i = 0; i < 32; ++i) q[i] = amax == 0.0f ? 0 : (int8_t)(int)roundf(b[i] / (float)orc_f16_to_f64(orc_f32_to_f16(d)));"),
+    "d4_dx_read_as_fp16": ("            dx = (double)d32;", "            dx = orc_f16_to_f64(rd16(grp + 4 * (b % 4)));"),
+    "d4_h_requantised_ds4": ("q8_1_row_layout(wtype == ORC_Q8_0_D4 ? ORC_D4 : ORC_DS4, h, F, hq8);",
+                             "q8_1_row_layout(ORC_DS4, h, F, hq8);"),
 }
 
 
@@ -66,6 +73,8 @@ def _pins(orc):
     yield lambda: tq.test_golden_rows(orc)
     yield lambda: tq.test_row_layout_against_numpy(orc, 256)
     yield lambda: tq.test_scatter_equals_gather(orc, 7)
+    yield lambda: tq.test_d4_rows_against_numpy(orc, 128)
+    yield lambda: tq.test_scatter_equals_gather_d4(orc, 7)
     yield lambda: tr.test_route_against_stable_sort(orc, 7, 16, 2)
     yield lambda: tr.test_route_weight_closed_forms(orc)
     yield lambda: tr.test_maps_against_brute_force(orc, 64, 4, 32, 31)
@@ -78,6 +87,8 @@ def _pins(orc):
         yield lambda w=w: tl.test_dense_special_case(orc, w)
         yield lambda w=w: tl.test_tiny_layer_against_numpy(orc, w)
     yield lambda: tl.test_combine_closed_forms(orc)
+    yield lambda: tg.test_row_dot_against_dequantised_fp64(orc, synth.Q8_0_D4)
+    yield lambda: tl.test_dense_special_case(orc, synth.Q8_0_D4)
 
 
 def _build_variant(tmp_path, name, before, after):

@@ -117,3 +117,46 @@ def test_scatter_equals_gather(orc, T):
     assert np.array_equal(g, want)
     z = m["slot"][(T // 2) * K:(T // 2) * K + K]
     assert not g[z].any()
+
+
+@pytest.mark.parametrize("n", [128, 2048])
+def test_d4_rows_against_numpy(orc, n):
+    """D4 (the layout the quantize-once page names for Q8_0): per 128 values the 4 blocks' fp32
+    d = amax/127, then the q of DS4.  Against numpy's float32 arithmetic, plus the links to the
+    pinned DS4 form: the same q bytes, and fp16 of the D4 d is DS4's d16."""
+    rng = np.random.default_rng(n + 5)
+    v = (rng.standard_normal((5, n)) * 3).astype(np.float32)
+    v[1, :32] = 0                       # an all-zero block: zero header, zero q
+    v[2, 32:64] = np.float32(1e-30)     # a tiny block: d far below fp16's range
+    v[3, 64] = np.float32(-1e7)         # d above fp16's largest finite value (DS4: d16 = inf)
+    got = orc.q8_1_rows(v, orc.D4)
+    assert np.array_equal(got, npref.q8_1_rows_d4(v))
+    ds4 = orc.q8_1_rows(v)
+    g = got.reshape(5, n // 128, 144)
+    h = ds4.reshape(5, n // 128, 144)
+    assert np.array_equal(g[:, :, 16:], h[:, :, 16:])
+    d = g[:, :, :16].copy().view("<f4").reshape(5, n // 32)
+    amax = np.abs(v.reshape(5, n // 32, 32)).max(axis=-1)
+    assert np.array_equal(d, (amax / np.float32(127)).astype(np.float32))
+    assert d[1, 0] == 0 and not g[1, 0, 16:48].any()
+    d16 = h[:, :, :16].copy().view("<u2").reshape(5, n // 32, 2)[..., 0]
+    assert np.array_equal(d.astype(np.float16).view(np.uint16), d16)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 600, 2099])
+def test_scatter_equals_gather_d4(orc, T):
+    """The page's scatter-equals-gather check for the D4 layout (10 of 512 experts, one
+    all-zero token), and both are numpy's D4 rows placed through src."""
+    rng = np.random.default_rng(200 + T)
+    H, K, E = 256, 10, 512
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[T // 2] = 0
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, _ = orc.route_topk(logits, K)
+    m = orc.build_maps(idx, E)
+    g = orc.quantize_gather(x, K, m["src"], orc.D4)
+    s = orc.quantize_scatter(x, K, m["slot"], orc.D4)
+    assert np.array_equal(g, s)
+    assert np.array_equal(g, npref.q8_1_rows_d4(x)[m["src"] // K])
+    z = m["slot"][(T // 2) * K:(T // 2) * K + K]
+    assert not g[z].any()
