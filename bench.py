@@ -289,6 +289,9 @@ def main():
     ap.add_argument("--walk-group-size", type=int, default=16)
     ap.add_argument("--gather-one", action="store_true",
                     help="streamed walk: one gather launch, wait and event per expert")
+    ap.add_argument("--act-d4", action="store_true",
+                    help="a Q8_0 workload with its activations in the D4 q8_1 layout (fp32 "
+                         "scales) instead of DS4")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -303,6 +306,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     c = synth.config_case(args.workload)
+    if args.act_d4:
+        if c.wtype != synth.Q8_0:
+            print("bench.py: --act-d4 applies to the Q8_0 workloads", file=sys.stderr)
+            sys.exit(2)
+        c.wtype = synth.Q8_0_D4          # the same experts, activations in D4
     layer = MoePrefillLayer(c.pool, c.expert_off, c.H, c.F, c.E, c.wtype, c.T, c.K,
                             group_size=16, ring_start=c.ring_start, device=dev)
     x = torch.from_numpy(c.x).to(dev)
@@ -401,7 +409,9 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}", "T": c.T, "H": c.H,
+        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}"
+                               + (", D4 activations" if c.wtype == synth.Q8_0_D4 else ""),
+                   "T": c.T, "H": c.H,
                    "F": c.F, "E": c.E, "K": c.K, "wtype": synth.WTYPE_NAME[c.wtype],
                    "group_size": 16, "active_experts": n_active, "stage_events": use_events},
         "roofline": roofline,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_GROUP 16     /* experts per group buffer ([G1] "What": MMQ_GROUP = 16) */
 #define MOE_MAX_E 2048       /* largest expert count the kernels accept */
 #define MOE_MAX_K 64         /* largest routes per token */
@@ -67,7 +67,17 @@ typedef enum {
     MOE_EHIP = -4           /* a HIP launch or runtime call failed */
 } moe_status;
 
-typedef enum { MOE_Q8_0 = 0, MOE_Q4_1 = 1 } moe_wtype;
+/* Weight type, and with it the q8_1 layout of the activations the MMQ reads: Q8_0 and Q4_1 take
+ * DS4 rows; MOE_Q8_0_D4 is Q8_0 weights taking D4 rows (the layout [QS] "Identity" names for Q8_0:
+ * per 128 values the 4 blocks' fp32 d, then their q, no s).  In the MMQ a D4 d enters the scale
+ * product as fp16(d) + fp16(d - fp16(d)), which carries d to within max(2^-22 d, 2^-25) while
+ * fp16(d) is finite (d <= 65504, a block's largest magnitude <= 8.3e6); beyond that the product
+ * overflows, as DS4's fp16 d does. */
+typedef enum { MOE_Q8_0 = 0, MOE_Q4_1 = 1, MOE_Q8_0_D4 = 2 } moe_wtype;
+
+/* moe_quantize_scatter_q8_1 mode bits */
+#define MOE_QUANT_PER_ROW 1   /* the per-row form (else: scatter) */
+#define MOE_QUANT_D4 2        /* D4 rows (else: DS4) */
 
 typedef enum {
     MOE_EPI_F32 = 0,           /* out = fp32 [rows x n_out] products (the down projection) */
@@ -104,9 +114,9 @@ int moe_build_maps(const int32_t *topk_idx, int T, int K, int E, int ring_start,
 
 /* a2  q8_1 quantisation of the layer input ([QS] opening section).
  * x fp32 [T x H] row-major; q8 [T*K x moe_q8_1_row_bytes(H)].
- * mode 0 (scatter): each token row is read once and written to rows slot[t*K+k], k < K.
- * mode 1 (per-row gather, the form the page replaces): row r quantises token src[r]/K.
- * Both write the same bytes. */
+ * mode without MOE_QUANT_PER_ROW (scatter): each token row is read once and written to rows
+ * slot[t*K+k], k < K.  With it (per-row gather, the form the page replaces): row r quantises
+ * token src[r]/K.  Both write the same bytes.  MOE_QUANT_D4: rows in the D4 layout. */
 int moe_quantize_scatter_q8_1(const float *x, int T, int H, int K, const int32_t *slot,
                               const int32_t *src, int mode, void *q8, void *stream);
 

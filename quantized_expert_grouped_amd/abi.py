@@ -15,7 +15,8 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_prefill.so")
 
-Q8_0, Q4_1 = 0, 1
+Q8_0, Q4_1, Q8_0_D4 = 0, 1, 2
+QUANT_PER_ROW, QUANT_D4 = 1, 2
 EPI_F32, EPI_SWIGLU_Q8_1, EPI_I32_BLOCKDOTS = 0, 1, 2
 WS_COUNTS, WS_OFFSETS, WS_SRC, WS_SLOT, WS_ORDER, WS_NACTIVE, WS_Q8X, WS_GROUPS, WS_HQ8, WS_DM, \
     WS_GROUP_STRIDE = range(11)

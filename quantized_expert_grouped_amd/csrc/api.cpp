@@ -45,7 +45,7 @@ const char* moe_strerror(int status) {
 }
 
 size_t moe_block_bytes(int wtype) {
-  return wtype == MOE_Q8_0 ? 34 : wtype == MOE_Q4_1 ? 20 : 0;
+  return wtype == MOE_Q8_0 || wtype == MOE_Q8_0_D4 ? 34 : wtype == MOE_Q4_1 ? 20 : 0;
 }
 
 size_t moe_expert_bytes(int H, int F, int wtype) {
@@ -111,8 +111,10 @@ int moe_build_maps(const int32_t* topk_idx, int T, int K, int E, int ring_start,
 
 int moe_quantize_scatter_q8_1(const float* x, int T, int H, int K, const int32_t* slot,
                               const int32_t* src, int mode, void* q8, void* stream) {
-  if (!x || !q8 || T < 1 || K < 1 || (mode != 0 && mode != 1)) return MOE_EINVAL;
-  if ((mode == 0 && !slot) || (mode == 1 && !src)) return MOE_EINVAL;
+  if (!x || !q8 || T < 1 || K < 1 || mode < 0 || mode > (MOE_QUANT_PER_ROW | MOE_QUANT_D4))
+    return MOE_EINVAL;
+  const bool per_row = (mode & MOE_QUANT_PER_ROW) != 0;
+  if ((!per_row && !slot) || (per_row && !src)) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(q8, 16)) return MOE_EINVAL;
   if (H < 128 || H % 128 != 0 || K > MOE_MAX_K) return MOE_EUNSUPPORTED;
   if ((long long)T * K > (1LL << 30)) return MOE_EUNSUPPORTED;
@@ -222,7 +224,8 @@ int moe_prefill_layer(const float* x, int T, int H, int F, int E, int K, const i
   mark(0);
   if ((e = launch_build_maps(topk_idx, T, K, E, ring_start, mo, s)) != hipSuccess) return MOE_EHIP;
   mark(1);
-  if ((e = launch_quantize(x, T, H, K, mo.slot, mo.src, 0, base + L.q8x, s)) != hipSuccess)
+  if ((e = launch_quantize(x, T, H, K, mo.slot, mo.src, act_mode_bits(wtype), base + L.q8x,
+                           s)) != hipSuccess)
     return MOE_EHIP;
   mark(2);
   if ((e = launch_gather_all_mmq(static_cast<const uint8_t*>(pool), expert_off, mo.order,
@@ -280,7 +283,8 @@ int moe_prefill_layer_packed(const float* x, int T, int H, int F, int E, int K,
              I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
              I32(L.ntiles), kMmqRows};
   if (launch_build_maps(topk_idx, T, K, E, ring_start, mo, s) != hipSuccess ||
-      launch_quantize(x, T, H, K, mo.slot, mo.src, 0, base + L.q8x, s) != hipSuccess)
+      launch_quantize(x, T, H, K, mo.slot, mo.src, act_mode_bits(wtype), base + L.q8x, s) !=
+          hipSuccess)
     return MOE_EHIP;
   MmqProblem gu{};
   gu.wtype = wtype;

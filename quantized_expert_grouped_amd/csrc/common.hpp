@@ -11,7 +11,7 @@ constexpr int kDs4Vals = 128;    // values per q8_1 group (4 blocks)
 constexpr int kDs4Bytes = 144;   // 16 B of (d, s) pairs + 128 B of q
 constexpr int kWave = 64;        // CDNA wavefront width
 
-__host__ __device__ constexpr int block_bytes(int wtype) { return wtype == 0 ? 34 : 20; }
+__host__ __device__ constexpr int block_bytes(int wtype) { return wtype == 1 ? 20 : 34; }
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);

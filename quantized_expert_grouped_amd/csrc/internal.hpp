@@ -41,6 +41,11 @@ hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_s
 inline int max_mtiles(int R, int E, int tile_rows) { return R / tile_rows + (E < R ? E : R); }
 
 // ---- a2 quantise ----------------------------------------------------------------------------
+constexpr int kQuantPerRow = 1;  // mode bit: the per-row form (else scatter)
+constexpr int kQuantD4 = 2;      // mode bit: the D4 layout (else DS4)
+// The weight type that reads D4 activations (Q8_0 weights).
+constexpr int kWtQ8_0D4 = 2;
+inline int act_mode_bits(int wtype) { return wtype == kWtQ8_0D4 ? kQuantD4 : 0; }
 hipError_t launch_quantize(const float* x, int T, int H, int K, const int32_t* slot,
                            const int32_t* src, int mode, uint8_t* q8, hipStream_t s);
 

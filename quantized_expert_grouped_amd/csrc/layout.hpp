@@ -14,7 +14,10 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
-inline bool valid_wtype(int wt) { return wt == MOE_Q8_0 || wt == MOE_Q4_1; }
+inline bool valid_wtype(int wt) { return wt == MOE_Q8_0 || wt == MOE_Q4_1 || wt == MOE_Q8_0_D4; }
+static_assert(MOE_Q8_0_D4 == kWtQ8_0D4 && MOE_QUANT_PER_ROW == kQuantPerRow &&
+                  MOE_QUANT_D4 == kQuantD4,
+              "the ABI's constants and the kernels' agree");
 
 // Region offsets of the layer's workspace (each 256-byte aligned).
 struct Layout {

@@ -63,7 +63,7 @@ constexpr int kAInstr = kRowsM * kARow / (64 * 16);  // 9 DMA instructions per s
 // tile-stages, copied verbatim into LDS rows 0..63 and 64..127.
 template <int WT>
 struct Geo {
-  static constexpr int kBRow = WT == 0 ? 4 * 34 : 4 * 20;          // bytes of a row per stage
+  static constexpr int kBRow = WT == 1 ? 4 * 20 : 4 * 34;          // bytes of a row per stage
   static constexpr int kTilePieces = 64 * kBRow / 16;              // 16-byte pieces per tile-stage
   static constexpr int kBInstr = 2 * kTilePieces / 64;             // 17 or 10
   static constexpr int kBPerWave = (kBInstr + 3) / 4;              // 5 or 3
@@ -190,17 +190,21 @@ __device__ __forceinline__ v4i b_raw(const uint8_t* brow, int b, int half) {
 
 template <int WT>
 __device__ __forceinline__ v4i b_unpack(const v4i& r) {
-  if (WT == 0) return r;
+  if (WT != 1) return r;
   const uint32_t m = 0x0f0f0f0fu, x0 = (uint32_t)r[0], x1 = (uint32_t)r[1];
   return (v4i){(int)(x0 & m), (int)(x1 & m), (int)((x0 >> 4) & m), (int)((x1 >> 4) & m)};
 }
 
 // The f16 MFMA operand of a row's weight headers: Q4_1 (d_b, m_b) in fp16 slots 2b, 2b+1;
-// Q8_0 d_b in slot b (slots 4..7 zero).
+// Q8_0 d_b in slot b (slots 4..7 zero); Q8_0 read with D4 activations: d_b in slots 2b and 2b+1
+// (they meet the two fp16 halves of the activation's fp32 d).
 template <int WT>
 __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
   if (WT == 1) return *reinterpret_cast<const v4i*>(brow);
   const uint2 d = *reinterpret_cast<const uint2*>(brow);
+  if (WT == kWtQ8_0D4)
+    return (v4i){(int)((d.x & 0xffffu) | (d.x << 16)), (int)((d.x >> 16) | (d.x & 0xffff0000u)),
+                 (int)((d.y & 0xffffu) | (d.y << 16)), (int)((d.y >> 16) | (d.y & 0xffff0000u))};
   return (v4i){(int)d.x, (int)d.y, 0, 0};
 }
 
@@ -303,11 +307,20 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
       }
       const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x0), izero, 0, 0, 0);
       const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x1), izero, 0, 0, 0);
-      // 2 * dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero)
-      if (WT == 1)
+      // 2 * dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero).  D4's fp32
+      // dx_b goes in as two fp16 (hi = fp16(dx), lo = fp16(dx - hi)) in slots 2b, 2b+1, both
+      // facing dw_b: the MFMA adds hi*dw + lo*dw, each product exact in fp32
+      if (WT == 1) {
         za[b][b] = (int)((uint32_t)hx[b] & 0xffffu);
-      else
+      } else if (WT == kWtQ8_0D4) {
+        const float dx = __int_as_float(hx[b]);
+        const _Float16 hi = (_Float16)dx;
+        const _Float16 lo = (_Float16)(dx - (float)hi);
+        za[b][b] = (int)((uint32_t)__builtin_bit_cast(uint16_t, hi) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
+      } else {
         za[b][b >> 1] = (b & 1) ? (int)((uint32_t)hx[b] << 16) : (int)((uint32_t)hx[b] & 0xffffu);
+      }
       const v8h sx = __builtin_bit_cast(v8h, za[b]);
       const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
       const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw1, fzero, 0, 0, 0);
@@ -407,7 +420,8 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
     *reinterpret_cast<uint4*>(dst + hoff + 16 + (fb & 3) * 32 + 16 * part) =
         make_uint4(qw[0], qw[1], qw[2], qw[3]);
     if (part == 0) {
-      const uint32_t hdr = nz ? (f2h(d) | (q8_1_scale_bits(d, S) << 16)) : 0u;
+      const uint32_t hdr =
+          !nz ? 0u : WT == kWtQ8_0D4 ? __float_as_uint(d) : (f2h(d) | (q8_1_scale_bits(d, S) << 16));
       *reinterpret_cast<uint32_t*>(dst + hoff + (fb & 3) * 4) = hdr;
     }
     if (p.debug_h != nullptr) {
@@ -478,6 +492,11 @@ hipError_t launch_mmq(const MmqProblem& p, hipStream_t s) {
     if (p.epilogue == 0) return launch_typed<0, 0>(p, s);
     if (p.epilogue == 1) return launch_typed<0, 1>(p, s);
     return launch_typed<0, 2>(p, s);
+  }
+  if (p.wtype == kWtQ8_0D4) {
+    if (p.epilogue == 0) return launch_typed<kWtQ8_0D4, 0>(p, s);
+    if (p.epilogue == 1) return launch_typed<kWtQ8_0D4, 1>(p, s);
+    return launch_typed<kWtQ8_0D4, 2>(p, s);
   }
   if (p.epilogue == 0) return launch_typed<1, 0>(p, s);
   if (p.epilogue == 1) return launch_typed<1, 1>(p, s);

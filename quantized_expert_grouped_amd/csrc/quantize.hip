@@ -6,7 +6,8 @@
 // Block arithmetic (identical in both forms): amax = max|v|; d = amax/127 (IEEE division);
 // q = roundf(v/d) (IEEE division, ties away from zero); S = sum q; stored d16 = fp16(d),
 // s16 = fp16(d * S); an all-zero block stores zeros.  Row layout (DS4): 144 B per 128 values =
-// 4 x (d16, s16) then 4 x 32 q.
+// 4 x (d16, s16) then 4 x 32 q.  The D4 layout, which the page names for Q8_0, keeps the 4
+// blocks' fp32 d in the same 16 header bytes instead (the same q, no s).
 //
 // One wavefront per token (scatter) or per row (per-row form).  A lane owns 16 consecutive
 // values (four coalesced float4 loads), so a block of 32 is a lane pair: one xor-shuffle for
@@ -21,7 +22,7 @@ namespace moe {
 
 namespace {
 
-template <int MODE>
+template <int MODE, int D4>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ x, int T, int H,
                                                        int K, const int32_t* __restrict__ slot,
                                                        const int32_t* __restrict__ src,
@@ -79,7 +80,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       qw[i] = packed;
     }
     S += __shfl_xor(S, 1);
-    const uint32_t hdr = nz ? (f2h(d) | (q8_1_scale_bits(d, S) << 16)) : 0u;
+    const uint32_t hdr =
+        !nz ? 0u : D4 ? __float_as_uint(d) : (f2h(d) | (q8_1_scale_bits(d, S) << 16));
     const uint32_t h1 = __shfl_down(hdr, 2);
     const uint32_t h2 = __shfl_down(hdr, 4);
     const uint32_t h3 = __shfl_down(hdr, 6);
@@ -111,12 +113,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
 hipError_t launch_quantize(const float* x, int T, int H, int K, const int32_t* slot,
                            const int32_t* src, int mode, uint8_t* q8, hipStream_t s) {
-  const int nunits = mode == 0 ? T : T * K;
+  const bool gather = (mode & kQuantPerRow) != 0, d4 = (mode & kQuantD4) != 0;
+  const int nunits = gather ? T * K : T;
   const dim3 grid((nunits + 3) / 4), block(256);
-  if (mode == 0)
-    quantize_kernel<0><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
+  if (!gather && !d4)
+    quantize_kernel<0, 0><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
+  else if (!gather)
+    quantize_kernel<0, 1><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
+  else if (!d4)
+    quantize_kernel<1, 0><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
   else
-    quantize_kernel<1><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
+    quantize_kernel<1, 1><<<grid, block, 0, s>>>(x, T, H, K, slot, src, q8);
   return hipGetLastError();
 }
 

@@ -236,7 +236,7 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
       !ok(hipMemcpyAsync(h_order, mo.order, (size_t)E * 4, hipMemcpyDeviceToHost, s)) ||
       !ok(hipMemcpyAsync(h_nact, mo.n_active, 4, hipMemcpyDeviceToHost, s)) ||
       !ok(hipEventRecord(w.routed, s)) ||
-      !ok(launch_quantize(x, T, H, K, mo.slot, mo.src, 0, base + L.q8x, s)) ||
+      !ok(launch_quantize(x, T, H, K, mo.slot, mo.src, act_mode_bits(wtype), base + L.q8x, s)) ||
       !ok(hipEventSynchronize(w.routed)))
     return MOE_EHIP;
   ++w.stats[kStSyncs];

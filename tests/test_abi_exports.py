@@ -41,9 +41,11 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert abi.abi_version() == 4
+    assert abi.abi_version() == 5
     assert abi.block_bytes(abi.Q8_0) == 34 and abi.block_bytes(abi.Q4_1) == 20
     assert abi.block_bytes(7) == 0
+    assert abi.block_bytes(abi.Q8_0_D4) == 34
+    assert abi.expert_bytes(2048, 512, abi.Q8_0_D4) == abi.expert_bytes(2048, 512, abi.Q8_0)
     assert abi.expert_bytes(2048, 512, abi.Q8_0) == 3342336
     assert abi.expert_bytes(2048, 512, abi.Q4_1) == 1966080
     assert abi.q8_1_row_bytes(2048) == 2304
@@ -101,7 +103,7 @@ def test_host_validation_rejects_before_any_launch():
                 E=16, group_size=16, ring_start=0, ws=ws, out=out, stream=0)
     assert abi.raw_prefill_layer(**{**args, "group_size": 0}) == -1
     assert abi.raw_prefill_layer(**{**args, "ring_start": 16}) == -1
-    assert abi.raw_prefill_layer(**{**args, "wtype": 2}) == -2
+    assert abi.raw_prefill_layer(**{**args, "wtype": 7}) == -2
     assert abi.raw_prefill_layer(**args, ws_bytes=100) == -3
     assert abi.raw_prefill_layer(**{**args, "x": T((7, 256), p=260)}) == -1   # misaligned x
     assert eb == 104448

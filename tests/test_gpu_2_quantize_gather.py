@@ -31,6 +31,27 @@ def test_quantize_both_modes_bit_exact(orc, T, H, K, E):
     assert np.array_equal(g1, want)
 
 
+@pytest.mark.parametrize("T,H,K,E", [(1, 256, 10, 512), (7, 256, 2, 16), (600, 2048, 10, 512),
+                                     (2099, 1152, 10, 512)])
+def test_quantize_d4_both_modes_bit_exact(orc, T, H, K, E):
+    """The same identity for the D4 layout (fp32 d per block, the layout the page names for
+    Q8_0), both forms against the oracle's bytes."""
+    note(f"quantize D4 T={T} H={H} K={K}")
+    rng = np.random.default_rng(T * H + K + 1)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[T // 2] = 0.0
+    if T > 3:
+        x[1] *= np.float32(1e-30)
+        x[2, :64] = np.round(x[2, :64] * 4) / 4
+    idx, _ = orc.route_topk(rng.standard_normal((T, E)).astype(np.float32), K)
+    m = orc.build_maps(idx, E)
+    want = orc.quantize_scatter(x, K, m["slot"], orc.D4)
+    g0 = gpu_quantize(x, K, m["slot"], m["src"], abi.QUANT_D4)
+    g1 = gpu_quantize(x, K, m["slot"], m["src"], abi.QUANT_D4 | abi.QUANT_PER_ROW)
+    assert np.array_equal(g0, want)
+    assert np.array_equal(g1, want)
+
+
 def test_quantize_full_t32k_sampled(orc):
     """T = 32768, H = 2048, K = 10 (input larger than the on-chip cache): the whole buffer in both
     modes is compared byte for byte with the oracle on 512 sampled tokens' rows, and the two modes

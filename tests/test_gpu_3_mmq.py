@@ -19,7 +19,7 @@ def _setup(orc, wtype, T, H, F, E, K, seed, skew=None):
                         zipf=skew)
     idx, _ = orc.route_topk(c.logits, K)
     m = orc.build_maps(idx, E)
-    q8x = orc.quantize_scatter(c.x, K, m["slot"])
+    q8x = orc.quantize_scatter(c.x, K, m["slot"], orc.act_layout(wtype))
     # group buffer: positions 0..n-1 hold experts in a shuffled order, in the MMQ layout
     experts = np.random.default_rng(seed).permutation(E)[:min(E, 16)].astype(np.int32)
     stride = c.expert_stride
@@ -31,14 +31,25 @@ def _setup(orc, wtype, T, H, F, E, K, seed, skew=None):
 def _abs_term_bound(wtype, wmat, n_out, k_in, act, dots):
     """Sum over blocks of |y_b| per (row, n): scales the fp32 accumulation's rounding error."""
     _, d, mm = npref.unpack_matrix(wmat, n_out, k_in, wtype)
-    _, dx, sx = npref.q8_1_decode(act, k_in)
+    _, dx, sx = (npref.q8_1_decode_d4 if wtype == synth.Q8_0_D4 else npref.q8_1_decode)(act, k_in)
     t = np.abs(dots.astype(np.float64)) * dx[:, None, :] * d[None, :, :]
     if mm is not None:
         t = t + np.abs(mm[None, :, :] * sx[:, None, :])
     return t.sum(axis=2)
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+def _d4_scale_bound(wtype, wmat, n_out, k_in, act, dots):
+    """D4 only: the kernel carries each fp32 d as fp16(d) + fp16(d - fp16(d)), within
+    max(2^-22 d, 2^-25) of d; this bounds what that moves sum_b y_b (twice, for margin)."""
+    if wtype != synth.Q8_0_D4:
+        return 0.0
+    _, d, _ = npref.unpack_matrix(wmat, n_out, k_in, wtype)
+    _, dx, _ = npref.q8_1_decode_d4(act, k_in)
+    e = np.maximum(dx * 2.0 ** -22, 2.0 ** -25)
+    return 2 * (np.abs(dots.astype(np.float64)) * e[:, None, :] * np.abs(d)[None, :, :]).sum(axis=2)
+
+
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 @pytest.mark.parametrize("shape", [(150, 512, 256, 12, 3, None), (700, 256, 128, 16, 2, 1.5)])
 def test_mmq_block_dots_bit_exact(orc, wtype, shape):
     T, H, F, E, K, skew = shape
@@ -64,7 +75,7 @@ def test_mmq_block_dots_bit_exact(orc, wtype, shape):
     assert not got[~in_group].any()
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 @pytest.mark.parametrize("shape", [(150, 512, 256, 12, 3, None), (1300, 256, 128, 4, 1, 3.0)])
 def test_mmq_down_f32(orc, wtype, shape):
     """The down projection's fp32 rows (n_out = H, k_in = F) on random q8_1 rows of h."""
@@ -72,7 +83,7 @@ def test_mmq_down_f32(orc, wtype, shape):
     c, m, _, experts, gbuf = _setup(orc, wtype, T, H, F, E, K, seed=3 * T + wtype, skew=skew)
     R = T * K
     rng = np.random.default_rng(5)
-    hq8 = orc.q8_1_rows((rng.standard_normal((R, F)) * 0.3).astype(np.float32))
+    hq8 = orc.q8_1_rows((rng.standard_normal((R, F)) * 0.3).astype(np.float32), orc.act_layout(wtype))
     mat_off = 2 * F * (H // 32) * synth.BLOCK_BYTES[wtype]
     out = torch.zeros((R, H), dtype=torch.float32, device="cuda")
     note(f"mmq f32 wtype={wtype} shape={shape}")
@@ -88,10 +99,11 @@ def test_mmq_down_f32(orc, wtype, shape):
         want = orc.mmq_rows(wtype, wmat, H, F, hq8[r0:r1])
         dots = orc.block_dots(wtype, wmat, H, F, hq8[r0:r1])
         bound = _abs_term_bound(wtype, wmat, H, F, hq8[r0:r1], dots) * (nb + 2) * 2.0 ** -23
+        bound = bound + _d4_scale_bound(wtype, wmat, H, F, hq8[r0:r1], dots)
         assert np.all(np.abs(got[r0:r1] - want) <= bound + 1e-30), (j, e)
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1])
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
 def test_mmq_swiglu_q8_1(orc, wtype):
     T, H, F, E, K = 150, 512, 256, 12, 3
     c, m, q8x, experts, gbuf = _setup(orc, wtype, T, H, F, E, K, seed=11 + wtype)
@@ -114,7 +126,7 @@ def test_mmq_swiglu_q8_1(orc, wtype):
         # the kernel's h: fp32 accumulation of the same products
         assert np.max(np.abs(got_h[r0:r1] - h)) <= 1e-5 * max(np.max(np.abs(h)), 1e-30)
         # its q8_1 bytes are exactly the quantiser's bytes of that h
-        assert np.array_equal(got_hq[r0:r1], orc.q8_1_rows(got_h[r0:r1]))
+        assert np.array_equal(got_hq[r0:r1], orc.q8_1_rows(got_h[r0:r1], orc.act_layout(wtype)))
         checked += r1 - r0
     assert checked > 0
 

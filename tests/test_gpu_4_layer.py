@@ -35,6 +35,7 @@ CASES = [
     ("ragged_q4_1", 301, 512, 256, 24, 4, synth.Q4_1, None),
     ("skew", 403, 256, 384, 32, 3, synth.Q4_1, 1.2),
     ("wide", 64, 1024, 128, 8, 8, synth.Q8_0, None),
+    ("ragged_d4", 301, 512, 256, 24, 4, synth.Q8_0_D4, None),
 ]
 
 
