@@ -27,8 +27,9 @@
 //     hold one block of 32 features;
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
 // K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of LDS
-// buffers with direct global->LDS loads (global_load_lds_dwordx4), two stages ahead of the MFMAs
-// (a ring of three), so the registers hold no staged data and no VALU moves it.  The weights come
+// buffers with direct global->LDS loads (global_load_lds_dwordx4), three stages ahead of the
+// MFMAs for Q4_1 (a ring of four) and two for Q8_0 (a ring of three), so the registers hold no
+// staged data and no VALU moves it.  The weights come
 // from the group buffer's MMQ layout (64-row tiles of one stage, each contiguous, every row's
 // block headers first), so a workgroup's weight stage is two contiguous runs, and in LDS the
 // rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart, a stride at which the 8- and 16-byte fragment
@@ -73,6 +74,14 @@ template <int WT>
 struct alignas(16) StageBuf {
   uint8_t a[kRowsM * kARow];
   uint8_t b[kRowsN * Geo<WT>::kBRow];
+};
+
+// LDS stage buffers per workgroup: four for Q4_1 (19.5 KB each: two workgroups per CU still fit,
+// and three stages are in flight ahead of the MFMAs), three for Q8_0 (26.6 KB each).
+template <int WT>
+struct Ring {
+  static constexpr int kN = WT == 1 ? 4 : 3;
+  StageBuf<WT> buf[kN];
 };
 
 // s_waitcnt immediate for vmcnt(n) (0 <= n < 64) with the other counters left alone
@@ -210,7 +219,7 @@ __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
 
 template <int WT, int EPI>
 __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, StageBuf<WT>& L2,
-                                         const MmqProblem& p, const uint8_t* W, int row0,
+                                         StageBuf<WT>& L3, const MmqProblem& p, const uint8_t* W, int row0,
                                          int nrows, int ntile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -252,18 +261,22 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
 
 
   // One stage: wait until stage s is in LDS for every wave (which also means every wave is done
-  // with stage s-1, whose buffer `fill` then receives stage s+2), then its MFMAs.  The three
-  // buffers are distinct LDS objects used with fixed roles per unrolled step, so the compiler
-  // can tell the reads of one from the loads into another and keeps the loads in flight.
+  // with stage s-1, whose buffer `fill` then receives stage s + ring - 1), then its MFMAs.  The
+  // ring's buffers are distinct LDS objects used with fixed roles per unrolled step, so the
+  // compiler can tell the reads of one from the loads into another and keeps the loads in flight.
+  // With ahead = the stages already issued after s, waiting until at most ahead * kMin loads
+  // are outstanding completes stage s on every wavefront (loads retire in issue order).
   auto step = [&](int s, const StageBuf<WT>& cur, StageBuf<WT>& fill) {
     // (the raw block-dot epilogue also stores inside the loop, so it drains the counter)
-    const bool ahead = EPI != 2 && s + 1 < nstages;
-    if (ahead)
+    const int ahead = EPI == 2 ? 0 : min(Ring<WT>::kN - 2, nstages - 1 - s);
+    if (ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(vm_imm(2 * kMinDmaPerStage<WT>));
+    else if (ahead == 1)
       __builtin_amdgcn_s_waitcnt(vm_imm(kMinDmaPerStage<WT>));
     else
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
     __builtin_amdgcn_s_barrier();
-    if (s + 2 < nstages) issue(fill, s + 2);
+    if (s + Ring<WT>::kN - 1 < nstages) issue(fill, s + Ring<WT>::kN - 1);
     if (!live) return;
     const uint8_t* arow = cur.a + (32 * wr + l32) * kARow;
     const uint8_t* brow0 = cur.b + (32 * ct0 + l32) * Geo<WT>::kBRow;
@@ -345,10 +358,20 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   __builtin_amdgcn_s_barrier();        // ... and every other wave's, before the ring refills
   issue(L0, 0);
   if (nstages > 1) issue(L1, 1);
-  for (int s0 = 0; s0 < nstages; s0 += 3) {
-    step(s0, L0, L2);
-    if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
-    if (s0 + 2 < nstages) step(s0 + 2, L2, L1);
+  if (Ring<WT>::kN == 4) {
+    if (nstages > 2) issue(L2, 2);
+    for (int s0 = 0; s0 < nstages; s0 += 4) {
+      step(s0, L0, L3);
+      if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
+      if (s0 + 2 < nstages) step(s0 + 2, L2, L1);
+      if (s0 + 3 < nstages) step(s0 + 3, L3, L2);
+    }
+  } else {
+    for (int s0 = 0; s0 < nstages; s0 += 3) {
+      step(s0, L0, L2);
+      if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
+      if (s0 + 2 < nstages) step(s0 + 2, L2, L1);
+    }
   }
   if (EPI == 2) return;
   if (EPI == 1) {  // every wavefront is past its last stage: the ring becomes scratch
@@ -440,7 +463,7 @@ constexpr int kXcds = 8;
 
 template <int WT, int EPI>
 __global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
-  __shared__ StageBuf<WT> L0, L1, L2;
+  __shared__ Ring<WT> ring;
   const int ntl = gridDim.x;
   const int live = ntl * (p.tile_count > 0 ? p.tile_count : *p.n_tiles);
   const int id = blockIdx.x + ntl * blockIdx.y;
@@ -457,19 +480,20 @@ __global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
                                          ? p.wbase + p.w_off[t.expert]
                                          : p.wbase + (size_t)t.ordinal * p.pos_stride);
   if (((uintptr_t)W & 15) != 0) return;  // the direct-to-LDS loads need 16-byte alignment
-  mmq_tile<WT, EPI>(L0, L1, L2, p, W, t.row0, t.nrows, work % ntl);
+  mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[2], ring.buf[Ring<WT>::kN - 1], p, W,
+                    t.row0, t.nrows, work % ntl);
 }
 
 template <int WT, int EPI>
 __global__ __launch_bounds__(256, 2) void mmq_group_kernel(MmqProblem p) {
-  __shared__ StageBuf<WT> L0, L1, L2;
+  __shared__ Ring<WT> ring;
   const int j = blockIdx.z;
   const int e = p.experts[j];
   const int r0 = p.offsets[e], cnt = p.offsets[e + 1] - r0;
   const uint8_t* W = p.wbase + (size_t)j * p.pos_stride + p.mat_offset;
   for (int m = blockIdx.y; m * kRowsM < cnt; m += gridDim.y)
-    mmq_tile<WT, EPI>(L0, L1, L2, p, W, r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM),
-                      blockIdx.x);
+    mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[2], ring.buf[Ring<WT>::kN - 1], p, W,
+                      r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM), blockIdx.x);
 }
 
 template <int WT, int EPI>
