@@ -93,13 +93,21 @@ __global__ __launch_bounds__(kScanThreads) void maps_scan_kernel(
   __shared__ int32_t s_til[kMaxE];   // ring position j -> its first m-tile
   __shared__ int32_t s_wsum[kScanThreads / 64 + 1];
   const int tid = threadIdx.x;
-  // per expert: exclusive prefix over chunks (in place), and the count
+  // per expert: exclusive prefix over chunks (in place), and the count; a batch of chunks'
+  // loads is issued before any of them is used, so the chain waits once per batch
+  constexpr int kBatch = 16;
   for (int e = tid; e < E; e += kScanThreads) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = hist[(size_t)c * E + e];
-      hist[(size_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        v[u] = c0 + u < nchunks ? hist[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (c0 + u < nchunks) hist[(size_t)(c0 + u) * E + e] = run;
+        run += v[u];
+      }
     }
     s_cnt[e] = run;
     s_off[e] = run;
