@@ -4,9 +4,9 @@
 // k ascending (fp32 fused multiply-adds in that fixed order, so the result depends only on the
 // token's own rows).
 //
-// One workgroup per token; each thread owns float4 columns of the row, reads the K routed rows
-// with 16-byte loads, up to 8 rows' loads in flight before their fused multiply-adds, and
-// writes the output once.
+// One workgroup per token; each thread owns float4 columns of the row (two at a time), reads the
+// K routed rows with 16-byte loads, up to 16 rows' loads per column in flight before their fused
+// multiply-adds, and writes the output once.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -16,7 +16,7 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kBatchK = 8;  // routed rows whose loads are in flight together
+constexpr int kBatchK = 16;  // routed rows whose loads are in flight together
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Dm,
                                                       const int32_t* __restrict__ slot,
@@ -31,29 +31,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   __syncthreads();
   const int n4 = H / 4;
-  for (int c = threadIdx.x; c < n4; c += 256) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
+  // two float4 columns per thread at a time (c and c + 256), so up to 2 * kBatchK loads are in
+  // flight before the first is used
+  for (int c = threadIdx.x; c < n4; c += 512) {
+    const bool two = c + 256 < n4;
+    v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < K; k0 += kBatchK) {
       // the loads of up to kBatchK rows first (each row is read once: non-temporal), then the
       // fused multiply-adds in k order
-      v4f d[kBatchK];
+      v4f d0[kBatchK], d1[kBatchK];
 #pragma unroll
-      for (int j = 0; j < kBatchK; ++j)
-        if (k0 + j < K)
-          d[j] = __builtin_nontemporal_load(
-              reinterpret_cast<const v4f*>(Dm + (size_t)s_row[k0 + j] * H) + c);
+      for (int j = 0; j < kBatchK; ++j) {
+        if (k0 + j < K) {
+          const v4f* row = reinterpret_cast<const v4f*>(Dm + (size_t)s_row[k0 + j] * H);
+          d0[j] = __builtin_nontemporal_load(row + c);
+          if (two) d1[j] = __builtin_nontemporal_load(row + c + 256);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < kBatchK; ++j) {
         if (k0 + j < K) {
           const float wk = s_w[k0 + j];
-          acc.x = fmaf(wk, d[j].x, acc.x);
-          acc.y = fmaf(wk, d[j].y, acc.y);
-          acc.z = fmaf(wk, d[j].z, acc.z);
-          acc.w = fmaf(wk, d[j].w, acc.w);
+          acc0.x = fmaf(wk, d0[j].x, acc0.x);
+          acc0.y = fmaf(wk, d0[j].y, acc0.y);
+          acc0.z = fmaf(wk, d0[j].z, acc0.z);
+          acc0.w = fmaf(wk, d0[j].w, acc0.w);
+          if (two) {
+            acc1.x = fmaf(wk, d1[j].x, acc1.x);
+            acc1.y = fmaf(wk, d1[j].y, acc1.y);
+            acc1.z = fmaf(wk, d1[j].z, acc1.z);
+            acc1.w = fmaf(wk, d1[j].w, acc1.w);
+          }
         }
       }
     }
-    __builtin_nontemporal_store(acc, reinterpret_cast<v4f*>(out + (size_t)t * H) + c);
+    v4f* o = reinterpret_cast<v4f*>(out + (size_t)t * H);
+    __builtin_nontemporal_store(acc0, o + c);
+    if (two) __builtin_nontemporal_store(acc1, o + c + 256);
   }
 }
 
