@@ -145,7 +145,8 @@ def test_layer_repeat_is_deterministic(orc):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[4]], ids=["tiny", "ragged_q4_1", "skew"])
+@pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[4], CASES[6]],
+                         ids=["tiny", "ragged_q4_1", "skew", "ragged_d4"])
 def test_layer_packed_pool_equals_gathered_layer(orc, case):
     """Experts kept in the MMQ layout and read in place (no gather): the same bytes reach the
     matmul, so the output is the gathered layer's bit for bit."""

@@ -14,9 +14,13 @@ from quantized_expert_grouped_amd.layer import MoePrefillLayer
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-@pytest.mark.parametrize("name", ["tiny", "t2k", "t8k", "t32k", "t30k_zipf"])
+@pytest.mark.parametrize("name", ["tiny", "t2k", "t8k", "t32k", "t30k_zipf", "t2k_d4"])
 def test_full_size_workload(orc, name):
-    c = synth.config_case(name)
+    if name.endswith("_d4"):                 # the same Q8_0 experts with D4 activations
+        c = synth.config_case(name[:-3])
+        c.wtype = synth.Q8_0_D4
+    else:
+        c = synth.config_case(name)
     layer = MoePrefillLayer(c.pool, c.expert_off, c.H, c.F, c.E, c.wtype, c.T, c.K,
                             group_size=16, ring_start=c.ring_start)
     x, logits = dev(c.x), dev(c.logits)
@@ -49,7 +53,7 @@ def test_full_size_workload(orc, name):
     xrb = abi.q8_1_row_bytes(H)
     o = abi.workspace_offset(abi.WS_Q8X, c.T, c.H, c.F, c.E, c.K, c.wtype, 16)
     q8 = ws[o:o + R * xrb].view(R, xrb)
-    rows = orc.q8_1_rows(c.x[ts])
+    rows = orc.q8_1_rows(c.x[ts], orc.act_layout(c.wtype))
     for j, t in enumerate(ts):
         got_rows = host(q8[torch.as_tensor(m["slot"][t * c.K:(t + 1) * c.K].astype(np.int64),
                                            device="cuda")])

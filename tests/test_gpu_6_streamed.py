@@ -61,6 +61,7 @@ CASES = [
     ("tiny", 7, 256, 128, 16, 2, synth.Q8_0, None),
     ("ragged_q4_1", 301, 512, 256, 24, 4, synth.Q4_1, None),
     ("skew", 403, 256, 384, 48, 3, synth.Q4_1, 1.5),
+    ("d4", 120, 256, 128, 20, 3, synth.Q8_0_D4, 0.8),
 ]
 
 # n_slots, group_size, flags, resident pattern
