@@ -4,8 +4,10 @@
 // them with the softmax of those K logits.
 //
 // One wavefront per token: lane l holds logits l, l+64, ... in registers (coalesced loads); K
-// rounds of a wave-wide (value desc, id asc) argmax pick the experts; lane k keeps pick k and the
-// weights come from one wave-wide sum.
+// rounds of a wave-wide (value desc, id asc) argmax pick the experts (DPP steps inside each row of
+// 16 lanes, then the 4 rows' winners read into scalars: no LDS round trip on the chain); lane k
+// keeps pick k and the weights come from one wave-wide sum.  (value desc, id asc) is a strict
+// order on distinct ids, so the winner does not depend on the order of the comparisons.
 #include <math.h>
 
 #include "common.hpp"
@@ -18,6 +20,24 @@ namespace {
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
+
+// One step of the wave-wide argmax: each lane takes the better of its (v, id) and that of the lane
+// the DPP pattern CTRL names (a permutation inside each row of 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ void dpp_best(float& v, int& id) {
+  const float ov =
+      __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oid = __builtin_amdgcn_update_dpp(0, id, CTRL, 0xF, 0xF, false);
+  if (better(ov, oid, v, id)) {
+    v = ov;
+    id = oid;
+  }
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each row
 
 template <int VPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
@@ -47,14 +67,25 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
         bid = id;
       }
     }
+    // best within each row of 16 lanes (every lane of the row ends with it), then of the 4 rows
+    dpp_best<kDppXor1>(bv, bid);
+    dpp_best<kDppXor2>(bv, bid);
+    dpp_best<kDppHalfMirror>(bv, bid);
+    dpp_best<kDppMirror>(bv, bid);
+    {
+      float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+      int rid = __builtin_amdgcn_readlane(bid, 0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oid = __shfl_xor(bid, off);
-      if (better(ov, oid, bv, bid)) {
-        bv = ov;
-        bid = oid;
+      for (int r = 1; r < 4; ++r) {
+        const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+        const int oid = __builtin_amdgcn_readlane(bid, 16 * r);
+        if (better(ov, oid, rv, rid)) {
+          rv = ov;
+          rid = oid;
+        }
       }
+      bv = rv;
+      bid = rid;
     }
     if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
     if (lane == k) {
