@@ -102,11 +102,14 @@ def test_layer_token_permutation_equivariance(orc):
     assert np.array_equal(got, ref[p])
 
 
-@pytest.mark.parametrize("edge", ["T1", "K_eq_E", "E1", "one_expert_takes_all", "half_empty"])
+@pytest.mark.parametrize("edge", ["T1", "K_eq_E", "E1", "one_expert_takes_all", "half_empty",
+                                  "max_E_and_K"])
 def test_layer_edge_cases(orc, edge):
     T, H, F, E, K, wtype = 50, 256, 128, 8, 2, synth.Q8_0
     if edge == "T1":
         T = 1
+    if edge == "max_E_and_K":                 # E = 2048 and K = 64, the largest the ABI takes
+        T, H, E, K = 40, 128, 2048, 64
     if edge == "K_eq_E":
         E, K = 6, 6
     if edge == "E1":
