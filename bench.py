@@ -265,6 +265,48 @@ def packed_layer(args, c, layer, x, logits, out, dev):
     print(json.dumps(line))
 
 
+def graph_steps(args, c, layer, x, logits, out, dev):
+    """Routing + the layer captured once in a HIP graph (torch.cuda.CUDAGraph over the layer's
+    stream-ordered launches), then replayed; prints one JSON line."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(1, args.warmup)):
+            layer.step(x, logits, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step(x, logits, out)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    line = {
+        "metric": "routed rows/sec (TxK) for the MoE prefill layer, one HIP graph per step",
+        "value": round(c.T * c.K * args.steps / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}", "graph": True},
+        "roofline": None,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +331,9 @@ def main():
     ap.add_argument("--walk-group-size", type=int, default=16)
     ap.add_argument("--gather-one", action="store_true",
                     help="streamed walk: one gather launch, wait and event per expert")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (routing + the layer) in a HIP graph and time its "
+                         "replays (another line, not the headline)")
     ap.add_argument("--act-d4", action="store_true",
                     help="a Q8_0 workload with its activations in the D4 q8_1 layout (fp32 "
                          "scales) instead of DS4")
@@ -325,6 +370,9 @@ def main():
         return
     if args.walk == "packed":
         packed_layer(args, c, layer, x, logits, out, dev)
+        return
+    if args.graph:
+        graph_steps(args, c, layer, x, logits, out, dev)
         return
 
     for _ in range(args.warmup):

@@ -169,3 +169,35 @@ def test_layer_packed_pool_equals_gathered_layer(orc, case):
     for rs in (c.ring_start, 0):
         got = host(layer.forward_packed(dev(c.x), dev(idx), dev(w), ring_start=rs))
         assert np.array_equal(got, ref), rs
+
+
+def test_layer_step_in_a_hip_graph(orc):
+    """Routing + the layer captured in one HIP graph: every replay, with eager work and
+    synchronisations between the replays, equals the eager step bit for bit."""
+    c = synth.make_case("graph", T=257, H=256, F=128, E=24, K=4, wtype=synth.Q4_1, seed=12,
+                        zipf=0.9)
+    layer = _layer(c)
+    x, logits = dev(c.x), dev(c.logits)
+    note("layer step eager, then captured in a graph")
+    want = host(layer.step(x, logits))
+    out = torch.empty((c.T, c.H), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.step(x, logits, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step(x, logits, out)
+    for r in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = host(out)
+        assert np.array_equal(got, want), r
+        # eager work between the replays
+        host(layer.step(x, logits))
+    idx, w = orc.route_topk(c.logits, c.K)
+    assert rel_err(want, orc.prefill_layer(c.x, idx, w, c.wtype, c.pool, c.expert_off, c.F,
+                                           c.E)) <= TOL
