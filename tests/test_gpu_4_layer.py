@@ -36,6 +36,8 @@ CASES = [
     ("skew", 403, 256, 384, 32, 3, synth.Q4_1, 1.2),
     ("wide", 64, 1024, 128, 8, 8, synth.Q8_0, None),
     ("ragged_d4", 301, 512, 256, 24, 4, synth.Q8_0_D4, None),
+    ("three_stages", 150, 384, 384, 12, 3, synth.Q4_1, None),
+    ("three_stages_q8_0", 150, 384, 384, 12, 3, synth.Q8_0, None),
 ]
 
 

@@ -73,3 +73,21 @@ def test_full_size_workload(orc, name):
     for t in c.zero_tokens:
         assert not out[t].any()
     assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_1, synth.Q8_0])
+def test_large_expert_shape(orc, wtype):
+    """H = 7168, F = 2048 (56 and 16 stages of 128 values, 2048-row down tiles): the layer's rows
+    of sampled tokens against the oracle."""
+    c = synth.make_case("large", T=96, H=7168, F=2048, E=12, K=4, wtype=wtype, seed=71 + wtype,
+                        zero_tokens=(5,))
+    layer = MoePrefillLayer(c.pool, c.expert_off, c.H, c.F, c.E, c.wtype, c.T, c.K,
+                            group_size=16, ring_start=c.ring_start)
+    note(f"large shape H=7168 F=2048 wtype={wtype}")
+    idx, w = orc.route_topk(c.logits, c.K)
+    out = host(layer.forward(dev(c.x), dev(idx), dev(w)))
+    ts = [0, 5, 37, 95]
+    want = np.stack([orc.token_out(c.x[t], idx[t], w[t], c.wtype, c.pool, c.expert_off, c.F)
+                     for t in ts])
+    assert rel_err(out[ts], want) <= 1e-3
+    assert not out[5].any()
