@@ -11,8 +11,9 @@
 //
 // One wavefront per token (scatter) or per row (per-row form).  A lane owns 16 consecutive
 // values (four coalesced float4 loads), so a block of 32 is a lane pair: one xor-shuffle for
-// amax and one for S.  Each lane then stores its 16 q bytes with one 16-byte store per
-// destination row, and the first lane of each 8-lane group the group's 16-byte (d, s) header.
+// amax and one for S.  The chunk's 1152 output bytes (8 groups of 144) are then permuted across
+// the lanes so that each destination row takes two stores of consecutive 16-byte pieces, and
+// every 128-byte line is written whole by one instruction.
 #include <math.h>
 
 #include "common.hpp"
@@ -58,8 +59,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     }
   };
   auto quantize_chunk = [&](int c0, const float* v) {
-    const int v0 = c0 + lane * 16;
-    const bool act = v0 < H;
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
@@ -85,18 +84,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     const uint32_t h1 = __shfl_down(hdr, 2);
     const uint32_t h2 = __shfl_down(hdr, 4);
     const uint32_t h3 = __shfl_down(hdr, 6);
-    const int g = v0 / kDs4Vals;
-    const size_t hoff = (size_t)g * kDs4Bytes;
-    const size_t qoff = hoff + 16 + ((lane & 7) >> 1) * 32 + (lane & 1) * 16;
-    const uint4 qv = make_uint4(qw[0], qw[1], qw[2], qw[3]);
-    const uint4 hv = make_uint4(hdr, h1, h2, h3);
+    // The chunk's 8 groups are 72 consecutive 16-byte pieces of a row (a group: its header
+    // piece, then its 8 q pieces).  Lane l holds q piece l % 8 of group l / 8 and lanes 8g the
+    // headers; piece i goes out from lane i (i < 64), pieces 64..71 from lanes 0..7, so every
+    // 128-byte line of the row is written whole by one store instruction.
+    const int g0 = c0 / kDs4Vals;                       // the chunk's first group in the row
+    const int pg = lane / 9, pp = lane % 9;             // piece `lane`: group, part
+    const int src = 8 * pg + (pp == 0 ? 0 : pp - 1);
+    const uint32_t hx0 = __shfl(hdr, src), hx1 = __shfl(h1, src), hx2 = __shfl(h2, src),
+                   hx3 = __shfl(h3, src);
+    const uint32_t qx0 = __shfl(qw[0], src), qx1 = __shfl(qw[1], src), qx2 = __shfl(qw[2], src),
+                   qx3 = __shfl(qw[3], src);
+    const uint4 p0 = pp == 0 ? make_uint4(hx0, hx1, hx2, hx3) : make_uint4(qx0, qx1, qx2, qx3);
+    const uint4 p1 = make_uint4(__shfl(qw[0], 56 + (lane & 7)), __shfl(qw[1], 56 + (lane & 7)),
+                                __shfl(qw[2], 56 + (lane & 7)), __shfl(qw[3], 56 + (lane & 7)));
+    const int ngroups = min(8, (H - c0) / kDs4Vals);    // whole groups in this chunk
+    const int npieces = 9 * ngroups;
     for (int k = 0; k < nrows; ++k) {
       const int r = MODE == 0 ? __shfl(my_row, k) : my_row;
-      uint8_t* row = q8 + (size_t)r * rb;
-      if (act) {
-        *reinterpret_cast<uint4*>(row + qoff) = qv;
-        if ((lane & 7) == 0) *reinterpret_cast<uint4*>(row + hoff) = hv;
-      }
+      uint8_t* seg = q8 + (size_t)r * rb + (size_t)g0 * kDs4Bytes;
+      if (lane < npieces) *reinterpret_cast<uint4*>(seg + 16 * lane) = p0;
+      if (lane < 8 && 64 + lane < npieces) *reinterpret_cast<uint4*>(seg + 16 * (64 + lane)) = p1;
     }
   };
   for (int c0 = 0; c0 < H; c0 += 2 * 64 * 16) {
