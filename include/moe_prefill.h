@@ -240,10 +240,12 @@ typedef struct moe_walk moe_walk;
 /* Creates the walk's state for a caller-owned device ring of n_slots (>= 1) slots, slot_stride
  * bytes apart (a multiple of 256): a copy stream (default priority), MOE_WALK_EVENTS + 2 events,
  * a pinned host buffer for the routing read-back, and the slot map (every slot free).  The ring
- * must stay allocated until moe_walk_destroy.  *walk is set on MOE_OK. */
+ * must stay allocated until moe_walk_destroy has returned.  *walk is set on MOE_OK; MOE_EHIP if
+ * a HIP resource (or the host memory) could not be made. */
 int moe_walk_create(void *ring, int n_slots, size_t slot_stride, moe_walk **walk);
 
-/* Waits for the walk's copy stream, then frees what moe_walk_create made.  NULL is a no-op. */
+/* Waits for the walk's copies and for every gather that read its ring (the slots' events), then
+ * frees what moe_walk_create made; the ring may be freed after this returns.  NULL is a no-op. */
 int moe_walk_destroy(moe_walk *walk);
 
 /* The whole layer as moe_prefill_layer computes it, with the experts streamed as described above.

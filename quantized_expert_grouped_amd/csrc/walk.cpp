@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <new>
 #include <vector>
 
 #include "internal.hpp"
@@ -132,7 +133,11 @@ struct moe_walk {
 namespace {
 
 void release(moe_walk* w) {
+  // the copies, then every gather that read a ring slot (each batch's event follows its
+  // gather), so that the caller may free the ring once this returns
   if (w->copy) (void)hipStreamSynchronize(w->copy);
+  for (hipEvent_t& e : w->used)
+    if (e) (void)hipEventSynchronize(e);
   for (hipEvent_t& e : w->used)
     if (e) (void)hipEventDestroy(e);
   if (w->copied) (void)hipEventDestroy(w->copied);
@@ -150,7 +155,8 @@ int moe_walk_create(void* ring, int n_slots, size_t slot_stride, moe_walk** walk
   if (!ring || !walk || n_slots < 1 || slot_stride == 0 || slot_stride % 256 != 0 ||
       (uintptr_t)ring % 256 != 0)
     return MOE_EINVAL;
-  moe_walk* w = new moe_walk;
+  moe_walk* w = new (std::nothrow) moe_walk;
+  if (!w) return MOE_EHIP;
   w->ring = static_cast<uint8_t*>(ring);
   w->n_slots = n_slots;
   w->stride = slot_stride;
