@@ -166,7 +166,8 @@ int moe_combine(const float *Dm, const int32_t *slot, const float *topk_w, int T
 /* a1..a7  The whole layer: maps, quantise-scatter, every group's gather, MMQ gate/up with SwiGLU and
  * q8_1 requantisation, MMQ down into Dm, combine.
  * x fp32 [T x H]; topk_idx int32 / topk_w fp32 [T x K]; pool: the experts, expert e at byte
- * expert_off[e] (int64 [E], device) of expert_bytes = moe_expert_bytes(H, F, wtype).
+ * expert_off[e] (int64 [E], device) of expert_bytes = moe_expert_bytes(H, F, wtype).  The pool's
+ * size is not an argument: every routed expert's bytes lying inside it is the caller's duty.
  * group_size (1..16) and ring_start (0..E-1) set which experts share a group buffer; the output is
  * bit-identical for every choice ([G1] "What": the same bytes land in the same places; [G2] "What
  * changes": the products and their order are unchanged).  ws: moe_workspace_size(...) bytes.
@@ -182,7 +183,8 @@ int moe_prefill_layer(const float *x, int T, int H, int F, int E, int K,
  * pool that never leaves device memory can be put in the matmul's layout once, with
  * moe_gather_group_mmq, and read in place).  packed_pool: expert e in the MMQ layout at byte
  * expert_off[e] (int64 [E], device; multiples of 16: a tile whose weights are not 16-byte
- * aligned is skipped and its rows are unspecified).  The products, their order and so the
+ * aligned is skipped and its rows are unspecified; inside the pool: the caller's duty, as for
+ * moe_prefill_layer).  The products, their order and so the
  * output are those of moe_prefill_layer with the same arguments, bit for bit; ws as there
  * (moe_workspace_size with any group size; the group region is not used). */
 int moe_prefill_layer_packed(const float *x, int T, int H, int F, int E, int K,
