@@ -340,7 +340,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by token chunks with no exchange: each GPU would run its own "
               "chunk, so the one-GPU figure is the per-GPU rate)", file=sys.stderr)
         sys.exit(2)

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_EINVAL = -1,        /* a null pointer, a size out of range, inconsistent arguments */
-    MOE_EUNSUPPORTED = -2,  /* a valid request this build does not implement (H or F not a
+    MOE_EUNSUPPORTED = -2,  /* a valid request the library does not implement (H or F not a
                                multiple of 128, E > MOE_MAX_E, K > MOE_MAX_K, unknown type) */
     MOE_EWORKSPACE = -3,    /* the workspace is smaller than the matching *_workspace_size() */
     MOE_EHIP = -4           /* a HIP launch or runtime call failed */
