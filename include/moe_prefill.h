@@ -158,7 +158,8 @@ int moe_mmq_grouped(int wtype, const void *group_buf, size_t pos_stride, size_t 
                     const int32_t *offsets, int E, const void *act_q8, int epilogue, void *out,
                     float *debug_h, void *stream);
 
-/* a7  Combine ([CS] "What it does": the expert rows in Dm are unweighted; the combine weights them).
+/* a7  Combine ([CS] "What it does": Dm holds the expert rows without their routing weights, which
+ * the combine applies).
  * out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i], k ascending; Dm fp32 [T*K x H]. */
 int moe_combine(const float *Dm, const int32_t *slot, const float *topk_w, int T, int K, int H,
                 float *out, void *stream);
@@ -169,8 +170,8 @@ int moe_combine(const float *Dm, const int32_t *slot, const float *topk_w, int T
  * expert_off[e] (int64 [E], device) of expert_bytes = moe_expert_bytes(H, F, wtype).  The pool's
  * size is not an argument: every routed expert's bytes lying inside it is the caller's duty.
  * group_size (1..16) and ring_start (0..E-1) set which experts share a group buffer; the output is
- * bit-identical for every choice ([G1] "What": the same bytes land in the same places; [G2] "What
- * changes": the products and their order are unchanged).  ws: moe_workspace_size(...) bytes.
+ * bit-identical for every choice ([G1] "What": every byte reaches the position one copy per expert
+ * gives it; [G2] "What changes": neither the products nor their order change).  ws: moe_workspace_size(...) bytes.
  * out fp32 [T x H].  H, F multiples of 128; E <= 2048; K <= min(E, 64). */
 int moe_prefill_layer(const float *x, int T, int H, int F, int E, int K,
                       const int32_t *topk_idx, const float *topk_w, int wtype,
@@ -184,8 +185,8 @@ int moe_prefill_layer(const float *x, int T, int H, int F, int E, int K,
  * moe_gather_group_mmq, and read in place).  packed_pool: expert e in the MMQ layout at byte
  * expert_off[e] (int64 [E], device; multiples of 16: a tile whose weights are not 16-byte
  * aligned is skipped and its rows are unspecified; inside the pool: the caller's duty, as for
- * moe_prefill_layer).  The products, their order and so the
- * output are those of moe_prefill_layer with the same arguments, bit for bit; ws as there
+ * moe_prefill_layer).  The matmul sees the bytes moe_prefill_layer gathers, so the output is
+ * that call's with the same arguments, bit for bit; ws as there
  * (moe_workspace_size with any group size; the group region is not used). */
 int moe_prefill_layer_packed(const float *x, int T, int H, int F, int E, int K,
                              const int32_t *topk_idx, const float *topk_w, int wtype,
@@ -230,8 +231,8 @@ size_t moe_workspace_offset(int which, int T, int H, int F, int E, int K, int wt
  * never exceed one group), or when the next copy needs a ring slot that the open batch itself holds (a ring
  * smaller than a group).  After a group's last batch its MMQ gate/up and down launch on that
  * group's m-tiles, so a group's products overlap later groups' copies.  The output is
- * bit-identical to moe_prefill_layer's for the same arguments (the same bytes reach the same
- * positions; the products and their order are unchanged). */
+ * bit-identical to moe_prefill_layer's for the same arguments: every expert's bytes reach the
+ * position the layer gives them, and the matmuls are the same launches' arithmetic. */
 #define MOE_WALK_EVENTS 64
 #define MOE_WALK_GATHER_ONE 1      /* one expert per batch: one wait, launch and event per expert
                                       ([G2] "What changes", the opt-out) */

@@ -270,8 +270,8 @@ void orc_quantize_scatter(const float *x, int T, int H, int K, const int32_t *sl
 
 /* ---------------------------------------------------------------------------------------
  * a3  gather.  [G1] "What": one copy per expert (the per-expert form) of the expert's bytes
- * into its position in the MMQ group buffer; the batched form must land the same bytes in
- * the same places.  [G1] "What" (new test) and [G2] "What changes" (skipped ring entries):
+ * into its position in the MMQ group buffer; the batched form must leave the buffer byte for
+ * byte as the per-expert copies do.  [G1] "What" (new test) and [G2] "What changes" (skipped ring entries):
  * a batch may start mid-group, so positions begin at first_pos.
  * Pinned in tests/test_oracle_gather_dot.py.
  * ------------------------------------------------------------------------------------- */
@@ -425,7 +425,7 @@ void orc_mmq_rows(int wtype, const uint8_t *wmat, int n_out, int k_in, const uin
 
 /* ---------------------------------------------------------------------------------------
  * a4..a6  one routed row through one expert.  [QS] opening section: the down-projection
- * input is quantised to q8_1 again ("the down-projection quantizations").  The pages do not
+ * input is quantised to q8_1 again (the page lists these quantisations as unchanged).  The pages do not
  * name the activation; this reads it as SwiGLU: h_f = silu(g_f) * u_f with
  * silu(z) = z / (1 + e^-z), gate = the expert's first F rows, up = the next F, no bias.
  * g, u and h in fp64; h is stored fp32 and re-quantised along F with orc_q8_1_row; the down
@@ -450,8 +450,8 @@ void orc_expert_row(int wtype, const uint8_t *expert, int H, int F, const uint8_
 }
 
 /* ---------------------------------------------------------------------------------------
- * a7  combine.  [CS] "What it does": the expert output rows in Dm are unweighted and the
- * combine weights them.  out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i], k ascending, fp64,
+ * a7  combine.  [CS] "What it does": Dm holds the expert rows without their routing weights,
+ * which the combine applies.  out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i], k ascending, fp64,
  * stored fp32.  Pinned in tests/test_oracle_layer.py.
  * ------------------------------------------------------------------------------------- */
 void orc_combine(const double *Dm, const int32_t *slot, const float *w, int T, int K, int H,

@@ -1,7 +1,7 @@
 // a3  The group gather.  "#439 prefill: a group's expert gathers in one launch", "What": one
-// launch copies up to 16 experts into the MMQ group buffer (blockIdx.y = expert), and the same
-// bytes land in the same places as with one copy per expert; its test covers batches of 1-16,
-// positions starting mid-group and the unaligned / odd-size fallback.  "Prompt path: an MMQ
+// launch copies up to 16 experts into the MMQ group buffer (blockIdx.y = expert), and the buffer
+// ends up byte for byte as one copy per expert leaves it; the page's test checks batches of 1 to
+// 16, positions starting mid-group and the unaligned / odd-size fallback.  "Prompt path: an MMQ
 // group's experts gathered in one launch, after one wait, released by one event", "What
 // changes": the same, one launch per group.
 //

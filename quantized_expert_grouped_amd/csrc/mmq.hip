@@ -1,6 +1,6 @@
 // a4..a6  Grouped quantised matmul (MMQ) on q8_1 activations.  "Prompt path: an MMQ group's
-// experts gathered in one launch, after one wait, released by one event", "What changes": the
-// products of a group's experts and their order are unchanged by how the group is gathered;
+// experts gathered in one launch, after one wait, released by one event", "What changes": how
+// a group is gathered alters neither which products its experts compute nor their order;
 // "#1368 prefill: quantize each token's MoE input once and scatter it to its k rows", opening
 // section: the down projection's input is quantised to q8_1 again.
 //

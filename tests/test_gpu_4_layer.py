@@ -80,7 +80,7 @@ def test_layer_against_oracle(orc, case):
 
 
 def test_layer_bit_identical_over_group_size_and_ring_start(orc):
-    """The same bytes land in the same places whatever the grouping and where the ring walk
+    """Every byte reaches the same place whatever the grouping and wherever the ring walk
     starts: the output is bitwise identical."""
     c = synth.make_case("inv", T=257, H=256, F=256, E=40, K=5, wtype=synth.Q4_1, seed=5,
                         zipf=0.9)
