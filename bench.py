@@ -11,6 +11,15 @@ routed rows per second (T*K rows per step).  Prints one JSON line.
 Per-stage HIP events recorded on the layer's own stream give each kernel's duration; the
 dominant kernel's roofline fraction uses its algorithmic work (ops or bytes) per launch.  The
 CPU baseline times the plain C oracle on a bounded sample of the same workload.
+
+Other lines (not the headline; each prints its own JSON line):
+    --walk streamed [--ring-slots N] [--resident-frac f] [--gather-one] [--walk-group-size G]
+        routing + moe_prefill_layer_streamed: experts copied from a pinned host arena through a
+        ring of device slots; reports the host->device rate against PCIe 5.0 x16.
+    --walk packed       routing + moe_prefill_layer_packed (experts kept in the MMQ layout).
+    --graph             routing + the layer captured in one HIP graph and replayed.
+    --act-d4            a Q8_0 workload with D4 activations (fp32 scales).
+    --copy-probe-mib N  one plain copy before the steps (the traffic counters' calibration).
 """
 from __future__ import annotations
 
