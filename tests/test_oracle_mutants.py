@@ -54,6 +54,11 @@ MUTANTS = {
                            "uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 32) * G;"),
     "mmq_pack_row_major": ("uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;",
                            "uint8_t *dst = out + ((size_t)n * stages + t) * G;"),
+    "scatter_first_row_only": ("        for (int k = 1; k < K; ++k)\n            memcpy(q8 + (size_t)slot[(size_t)t * K + k] * rb, row, rb);",
+                               "        for (int k = 1; k < 1; ++k)\n            memcpy(q8 + (size_t)slot[(size_t)t * K + k] * rb, row, rb);"),
+    "combine_unweighted": ("acc += (double)w[(size_t)t * K + k] * Dm[(size_t)slot[(size_t)t * K + k] * H + i];",
+                           "acc += Dm[(size_t)slot[(size_t)t * K + k] * H + i];"),
+    "silu_dropped": ("h[f] = (float)(g / (1.0 + exp(-g)) * u);", "h[f] = (float)(g * u);"),
     "d4_header_fp16": ("memcpy(grp + 4 * j, &d, 4);",
                        "{ float dr = (float)orc_f16_to_f64(orc_f32_to_f16(d)); memcpy(grp + 4 * j, &dr, 4); }"),
     "d4_q_from_fp16_d": ("for (int i = 0; i < 32; ++i) q[i] = amax == 0.0f ? 0 : (int8_t)(int)roundf(b[i] / d);",
