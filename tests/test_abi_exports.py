@@ -125,3 +125,28 @@ def test_walk_host_validation():
     assert L.moe_walk_stats(None, None, 0) == -1
     assert L.moe_prefill_layer_streamed(None, 16, 4, 256, 128, 8, 2, 16, 16, 0, 16, 1 << 20, 16,
                                         16, 16, 0, 0, 16, 1 << 20, 16, None) == -1
+
+
+def test_packed_layer_host_validation():
+    L = abi.lib()
+    # x, T, H, F, E, K, idx, w, wtype, packed_pool, expert_off, expert_bytes, ring_start, ws,
+    # ws_bytes, out, stream
+    eb = abi.expert_bytes(256, 128, abi.Q8_0)
+    ok = [16, 4, 256, 128, 8, 2, 16, 16, abi.Q8_0, 256, 16, eb, 0, 256, 1 << 40, 16, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["x", "T", "H", "F", "E", "K", "idx", "w", "wtype", "pool", "off", "eb", "rs",
+                 "ws", "ws_bytes", "out", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.moe_prefill_layer_packed(*a)
+
+    assert call(pool=None) == -1                 # no pool
+    assert call(off=None) == -1                  # no offsets
+    assert call(wtype=7) == -2                   # unknown type
+    assert call(H=200) == -2                     # H % 128
+    assert call(eb=eb + 1) == -1                 # wrong expert size
+    assert call(pool=264) == -1                  # pool not 16-byte aligned
+    assert call(rs=8) == -1                      # ring_start >= E
+    assert call(ws_bytes=16) == -3               # workspace too small
