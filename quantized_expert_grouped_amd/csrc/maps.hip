@@ -32,13 +32,18 @@ __global__ __launch_bounds__(256) void maps_hist_kernel(const int32_t* __restric
   for (int e = lane; e < E; e += 64) h[e] = 0;
   __syncthreads();
   if (chunk < nchunks) {
+    // every step's ids are loaded before the first is counted: one load latency per chunk
     const int base = chunk * kMapChunk;
+    int ids[kMapChunk / 64];
+#pragma unroll
     for (int it = 0; it < kMapChunk / 64; ++it) {
       const int i = base + it * 64 + lane;
-      if (i < R) {
-        const int e = idx[i];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
-      }
+      ids[it] = i < R ? idx[i] : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < kMapChunk / 64; ++it) {
+      const int e = ids[it];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
     }
   }
   __syncthreads();
@@ -165,9 +170,16 @@ __global__ __launch_bounds__(256) void maps_scatter_kernel(const int32_t* __rest
   // From here each wavefront touches only its own counters; LDS operations of one wavefront
   // complete in issue order, so no further barrier is needed.
   const int base = chunk * kMapChunk;
+  int ids[kMapChunk / 64];  // every step's ids loaded up front: one load latency per chunk
+#pragma unroll
   for (int it = 0; it < kMapChunk / 64; ++it) {
     const int i = base + it * 64 + lane;
-    const int e = i < R ? idx[i] : -1;
+    ids[it] = i < R ? idx[i] : -1;
+  }
+#pragma unroll
+  for (int it = 0; it < kMapChunk / 64; ++it) {
+    const int i = base + it * 64 + lane;
+    const int e = ids[it];
     const bool valid = (unsigned)e < (unsigned)E;
     uint64_t peers = ballot(valid);
     for (int b = 0; b < nbits; ++b) {
