@@ -36,7 +36,10 @@
  *                             of 64 rows by 4 blocks: for tile j, stage t, row i < 64 (row 64j+i),
  *                             the row's blocks 4t..4t+3 take G = 4 * block bytes at byte
  *                             ((j * nblk/4 + t) * 64 + i) * G, headers first:
- *                               Q4_1 (G = 80) : (d, m) of the 4 blocks, then their qs[16]
+ *                               Q4_1 (G = 80) : (d, m) of the 4 blocks, then each block's 16
+ *                                               packed bytes in two halves: byte 8h + i holds
+ *                                               element 16h + i in its low nibble and element
+ *                                               16h + 8 + i in its high nibble
  *                               Q8_0 (G = 136): d of the 4 blocks, then their q[32]
  *   q8_1 row of n values    : n/128 groups of 144 B: (fp16 d, fp16 s) of its 4 blocks of 32, then
  *                             the 4 blocks' int8 q.  d = amax/127 (fp32), q = roundf(v/d), s = d*sum q

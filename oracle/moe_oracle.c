@@ -292,7 +292,11 @@ void orc_gather(const uint8_t *pool, const int64_t *expert_off, const int32_t *e
  *   a matrix of n_rows rows and nblk blocks per row, for tile j < n_rows/64, stage t < nblk/4,
  *   row i < 64 (matrix row 64j+i) holds blocks 4t..4t+3 of that row at byte
  *   ((j*(nblk/4) + t)*64 + i) * G, G = 4 * block bytes, as
- *     Q4_1 (G = 80) : (d, m) of the 4 blocks (16 B), then qs[16] of the 4 blocks (64 B)
+ *     Q4_1 (G = 80) : (d, m) of the 4 blocks (16 B), then 16 packed bytes of each block (64 B)
+ *                     in the order of two halves: byte 8h + i (h < 2, i < 8) holds element
+ *                     16h + i in its low nibble and element 16h + 8 + i in its high nibble
+ *                     (the raw block's byte j holds elements j and j + 16), so the elements
+ *                     16h..16h+15 of a block sit in one 8-byte half
  *     Q8_0 (G = 136): d of the 4 blocks (8 B), then q[32] of the 4 blocks (128 B)
  * The expert keeps its order gate | up | down and its size.  Positions in the group buffer are
  * as in orc_gather.
@@ -311,8 +315,17 @@ static void mmq_pack_matrix(int wtype, const uint8_t *raw, int n_rows, int nblk,
             uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;
             for (int j = 0; j < 4; ++j) {
                 if (wtype == ORC_Q4_1) {
+                    const uint8_t *qs = src + j * bb + 4;
+                    uint8_t v[32];                                    /* the block's elements */
+                    for (int e = 0; e < 16; ++e) {
+                        v[e] = qs[e] & 15;
+                        v[e + 16] = qs[e] >> 4;
+                    }
                     memcpy(dst + 4 * j, src + j * bb, 4);             /* d, m */
-                    memcpy(dst + 16 + 16 * j, src + j * bb + 4, 16);  /* qs */
+                    for (int h = 0; h < 2; ++h)
+                        for (int i = 0; i < 8; ++i)
+                            dst[16 + 16 * j + 8 * h + i] =
+                                (uint8_t)(v[16 * h + i] | (v[16 * h + 8 + i] << 4));
                 } else {
                     memcpy(dst + 2 * j, src + j * bb, 2);             /* d */
                     memcpy(dst + 8 + 32 * j, src + j * bb + 2, 32);   /* q */

@@ -77,7 +77,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_all_kernel(
 // group buffer holds every matrix as those tile-stages, each one contiguous: for tile j, stage
 // t and row i < 64 (matrix row 64j+i), the row's blocks 4t..4t+3 sit at byte
 // ((j * stages + t) * 64 + i) * G, G = 4 * block bytes, with the blocks' headers first:
-//   Q4_1, G = 80 : (d, m) of the 4 blocks, then their qs[16]
+//   Q4_1, G = 80 : (d, m) of the 4 blocks, then each block's 16 packed bytes in two halves:
+//                  byte 8h + i holds element 16h + i (low nibble) and 16h + 8 + i (high), so
+//                  elements 16h..16h+15 sit in one 8-byte half (raw byte j: elements j, j + 16)
 //   Q8_0, G = 136: d of the 4 blocks, then their q[32]
 // The expert keeps its order (gate | up | down) and its size.  A 64-row tile is one contiguous
 // run in the raw expert and one in the packed expert, so a workgroup moves a tile's rows for
@@ -96,23 +98,32 @@ struct Pack {
   static constexpr int kLds = 64 * kStages * kG;
 };
 
-// Byte offset, within a row's 4-block group in the raw layout, of the low half of output word k
-// of the packed group (the high half is 2 bytes further).  Every such offset is even.
-template <int WT>
-__device__ __forceinline__ int packed_word_src(int k) {
-  if (WT == 1) return k < 4 ? 20 * k : 20 * ((k - 4) >> 2) + 4 + 4 * ((k - 4) & 3);
+// Q8_0: byte offset, within a row's 4-block group in the raw layout, of the low half of output
+// word k of the packed group (the high half is 2 bytes further).  Every such offset is even.
+__device__ __forceinline__ int q8_0_word_src(int k) {
   if (k < 2) return 68 * k;  // (d_{2k}, d_{2k+1}) live at 68k and 68k + 34
   return 34 * ((k - 2) >> 3) + 2 + 4 * ((k - 2) & 7);
 }
 
-template <int WT>
-__device__ __forceinline__ uint32_t packed_word(const uint8_t* grp, int k) {
-  const int o = packed_word_src<WT>(k);
+__device__ __forceinline__ uint32_t q8_0_word(const uint8_t* grp, int k) {
+  const int o = q8_0_word_src(k);
   const uint16_t* h = reinterpret_cast<const uint16_t*>(grp);
-  if (WT == 1) return *reinterpret_cast<const uint32_t*>(grp + o);  // 4-byte aligned
   const uint32_t lo = h[o >> 1];
   const uint32_t hi = h[(k < 2 ? o + 34 : o + 2) >> 1];
   return lo | (hi << 16);
+}
+
+// Q4_1: 16-byte piece c < 5 of a packed group from the raw group (4-byte aligned): c = 0 the
+// blocks' (d, m), c >= 1 block c-1's packed bytes in the half order.  With the raw words
+// x0..x3 (bytes 0-3, 4-7, 8-11, 12-15), the half-0 bytes take the low nibbles of x0 | x1 and,
+// above them, those of x2 | x3; the half-1 bytes the high nibbles of the same words.
+__device__ __forceinline__ v4u q4_1_piece(const uint8_t* grp, int c) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(grp);
+  if (c == 0) return (v4u){w[0], w[5], w[10], w[15]};  // (d, m) of block u at byte 20u
+  const uint32_t* x = w + 5 * (c - 1) + 1;             // qs of block c-1 at byte 20(c-1) + 4
+  const uint32_t m = 0x0f0f0f0fu;
+  return (v4u){(x[0] & m) | ((x[2] & m) << 4), (x[1] & m) | ((x[3] & m) << 4),
+               ((x[0] >> 4) & m) | (x[2] & ~m), ((x[1] >> 4) & m) | (x[3] & ~m)};
 }
 
 // One work item: tile `tile` of matrix `mat` (0 gate, 1 up, 2 down), stages t0 .. t0+ns-1.
@@ -194,12 +205,18 @@ __device__ __forceinline__ void pack_item(const uint8_t* __restrict__ src_e,
   const bool wide = ((uintptr_t)d & 15) == 0;
   for (int q = tid; q < total16; q += kGatherThreads) {
     uint32_t v[4];
+    if (WT == 1) {  // a group is 5 whole pieces
+      const int st = q / (64 * 5), qq = q % (64 * 5);
+      const v4u p = q4_1_piece(lds + (qq / 5) * seg + st * G, qq % 5);
+      v[0] = p[0], v[1] = p[1], v[2] = p[2], v[3] = p[3];
+    } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int w = 4 * q + u;                    // word of the run
-      const int st = w / (64 * words), ww = w % (64 * words);
-      const int i = ww / words, k = ww % words;   // row of the tile, word of its group
-      v[u] = packed_word<WT>(lds + i * seg + st * G, k);
+      for (int u = 0; u < 4; ++u) {
+        const int w = 4 * q + u;                    // word of the run
+        const int st = w / (64 * words), ww = w % (64 * words);
+        const int i = ww / words, k = ww % words;   // row of the tile, word of its group
+        v[u] = q8_0_word(lds + i * seg + st * G, k);
+      }
     }
     if (wide) {
       __builtin_nontemporal_store((v4u){v[0], v[1], v[2], v[3]}, reinterpret_cast<v4u*>(d) + q);

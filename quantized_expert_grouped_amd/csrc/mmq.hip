@@ -32,10 +32,15 @@
 // staged data and no VALU moves it.  The weights come
 // from the group buffer's MMQ layout (64-row tiles of one stage, each contiguous, every row's
 // block headers first), so a workgroup's weight stage is two contiguous runs, and in LDS the
-// rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart, a stride at which the 8- and 16-byte fragment
-// reads of 32 rows hit distinct banks.  q8_1 rows keep their 144-byte groups.  Q4_1 nibbles are
-// split with two masks: a lane half h takes elements 8h..8h+7 and 16+8h..16+8h+7 of a block
-// (8 packed bytes), on both operands, so the int8 dot product is unchanged.
+// rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart.  q8_1 rows keep their 144-byte groups.  LDS
+// serves 8-byte reads 32 lanes and 16-byte reads 16 lanes at a time over 64 four-byte banks:
+// the 16-byte reads at both strides and Q8_0's 8-byte pairs are conflict-free; Q4_1's 8-byte
+// weight reads conflict 2-way (reading two blocks' halves with one 16-byte read instead
+// measured no faster).  A lane half h
+// takes elements 16h..16h+15 of a block on both operands: one 16-byte activation read (an
+// 8-byte pair 16 bytes apart would conflict 2-way on the 144-byte row stride) and, for Q4_1,
+// the block's 8-byte half h, whose low and high nibbles the gather arranged to be exactly
+// those elements, split with two masks.
 #include <math.h>
 
 #include "common.hpp"
@@ -60,7 +65,8 @@ constexpr int kAInstr = kRowsM * kARow / (64 * 16);  // 9 DMA instructions per s
 
 // Weights arrive in the MMQ layout the gather writes: each matrix as tiles of 64 rows by one
 // stage (4 blocks), every tile-stage contiguous, a row's 4 blocks headers first (Q4_1: 4 x (d, m)
-// then 4 x qs[16], 80 B; Q8_0: 4 x d then 4 x q[32], 136 B).  A workgroup's stage is two such
+// then 4 x 16 packed bytes, each block's byte 8h + i holding elements 16h + i and 16h + 8 + i,
+// 80 B; Q8_0: 4 x d then 4 x q[32], 136 B).  A workgroup's stage is two such
 // tile-stages, copied verbatim into LDS rows 0..63 and 64..127.
 template <int WT>
 struct Geo {
@@ -158,21 +164,14 @@ __device__ __forceinline__ void issue_stage(StageBuf<WT>& S, const DmaPlan<WT>& 
   }
 }
 
-// int8 MFMA operands of block b.  Q4_1: lane half h takes elements 8h..8h+7, 16+8h..16+8h+7.
-// Q8_0: lane half h takes elements 16h..16h+15.
+// int8 MFMA operands of block b: lane half h takes elements 16h..16h+15 of both operands.
 template <int WT>
 __device__ __forceinline__ v4i a_frag(const uint8_t* arow, int b, int half) {
-  const uint8_t* q = arow + 16 + 32 * b;
-  if (WT == 1) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(q + 8 * half);
-    const uint2 hi = *reinterpret_cast<const uint2*>(q + 16 + 8 * half);
-    return (v4i){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-  }
-  return *reinterpret_cast<const v4i*>(q + 16 * half);
+  return *reinterpret_cast<const v4i*>(arow + 16 + 32 * b + 16 * half);
 }
 
-// Weight operand of block b from a row's stage bytes (headers first).  Rows are 80 or 136 bytes
-// apart, so 8- and 16-byte reads of 32 consecutive rows hit distinct LDS banks.
+// Weight operand of block b from a row's stage bytes (headers first).  Q4_1: the block's packed
+// half h, low nibbles = elements 16h..16h+7, high nibbles = 16h+8..16h+15.
 template <int WT>
 __device__ __forceinline__ v4i b_frag(const uint8_t* brow, int b, int half) {
   if (WT == 1) {

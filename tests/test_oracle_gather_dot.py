@@ -29,8 +29,9 @@ def test_gather_is_per_expert_copy(orc):
 def _decode_mmq_matrix(packed, wtype, n_rows, nblk):
     """Blocks (d, m, q) in raw block order, read from one MMQ-layout matrix by the layout's
     description: tile j of 64 rows, stage t of 4 blocks, row i -> one 4-block group at
-    ((j * nblk/4 + t) * 64 + i) * G; Q4_1 G = 80: 4 x (d, m) then 4 x qs[16]; Q8_0 G = 136:
-    4 x d then 4 x q[32]."""
+    ((j * nblk/4 + t) * 64 + i) * G; Q4_1 G = 80: 4 x (d, m) then 4 x 16 packed bytes, byte
+    8h + i holding element 16h + i (low nibble) and 16h + 8 + i (high); Q8_0 G = 136: 4 x d
+    then 4 x q[32]."""
     G = 136 if wtype == synth.Q8_0 else 80
     g = np.asarray(packed, np.uint8).reshape(n_rows // 64, nblk // 4, 64, G)
     g = g.transpose(0, 2, 1, 3).reshape(n_rows * nblk // 4, G)   # row-major groups
@@ -39,8 +40,9 @@ def _decode_mmq_matrix(packed, wtype, n_rows, nblk):
         q = g[:, 8:136].reshape(-1, 32).view(np.int8).astype(np.int64)
         return d, None, q
     hdr = g[:, 0:16].copy().view("<u2").reshape(-1, 4, 2)
-    qs = g[:, 16:80].reshape(-1, 16).astype(np.int64)
-    return hdr[:, :, 0].reshape(-1), hdr[:, :, 1].reshape(-1), np.concatenate([qs & 15, qs >> 4], 1)
+    qs = g[:, 16:80].reshape(-1, 2, 8).astype(np.int64)        # (block, half, byte)
+    q = np.concatenate([qs & 15, qs >> 4], 2).reshape(-1, 32)   # half h: 16h..16h+7, 16h+8..
+    return hdr[:, :, 0].reshape(-1), hdr[:, :, 1].reshape(-1), q
 
 
 def _decode_mmq(packed, wtype, H, F):

@@ -46,8 +46,10 @@ MUTANTS = {
                                           "group_buf + (size_t)j * pos_stride);"),
     "down_at_up_offset": ("const uint8_t *down = expert + (size_t)2 * F * gu_row;",
                           "const uint8_t *down = expert + (size_t)F * gu_row;"),
-    "mmq_pack_q_shifted": ("memcpy(dst + 16 + 16 * j, src + j * bb + 4, 16);  /* qs */",
-                           "memcpy(dst + 16 + 16 * j, src + j * bb + 3, 16);  /* qs */"),
+    "mmq_pack_q_shifted": ("const uint8_t *qs = src + j * bb + 4;",
+                           "const uint8_t *qs = src + j * bb + 3;"),
+    "mmq_pack_half_nibbles_swapped": ("(uint8_t)(v[16 * h + i] | (v[16 * h + 8 + i] << 4));",
+                                      "(uint8_t)(v[16 * h + 8 + i] | (v[16 * h + i] << 4));"),
     "mmq_pack_d_order": ("memcpy(dst + 2 * j, src + j * bb, 2);             /* d */",
                          "memcpy(dst + 6 - 2 * j, src + j * bb, 2);         /* d */"),
     "mmq_pack_tile_rows": ("uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;",
