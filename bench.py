@@ -19,6 +19,8 @@ Other lines (not the headline; each prints its own JSON line):
     --walk packed       routing + moe_prefill_layer_packed (experts kept in the MMQ layout).
     --graph             routing + the layer captured in one HIP graph and replayed.
     --act-d4            a Q8_0 workload with D4 activations (fp32 scales).
+    --cold-mib N        cold cache: N MiB of scratch written between steps (512 or more flushes
+                        the 256 MB MALL and the L2s), each step timed by events around it.
     --copy-probe-mib N  one plain copy before the steps (the traffic counters' calibration).
 """
 from __future__ import annotations
@@ -343,6 +345,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture one step (routing + the layer) in a HIP graph and time its "
                          "replays (another line, not the headline)")
+    ap.add_argument("--cold-mib", type=int, default=0,
+                    help="write this many MiB of scratch between steps (cache flush) and time "
+                         "each step with events around it (another line, not the headline)")
     ap.add_argument("--act-d4", action="store_true",
                     help="a Q8_0 workload with its activations in the D4 q8_1 layout (fp32 "
                          "scales) instead of DS4")
@@ -393,9 +398,17 @@ def main():
         abi.profile_begin(args.steps)
         ev_route = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                     for _ in range(args.steps)]
+    flush = None
+    if args.cold_mib > 0:
+        flush = torch.empty(args.cold_mib << 20, dtype=torch.uint8, device=dev)
+        ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)          # evicts the previous step's data from the caches
+            ev_step[i][0].record(stream)
         if use_events:
             ev_route[i][0].record(stream)
             idx, w = layer.route(logits)
@@ -403,12 +416,17 @@ def main():
             layer.forward(x, idx, w, out)
         else:
             layer.step(x, logits, out)
+        if flush is not None:
+            ev_step[i][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     ms_per_step = elapsed * 1e3 / args.steps
     rows = c.T * c.K
     value = rows * args.steps / elapsed
+    if flush is not None:                  # the steps alone, without the flushes
+        ms_per_step = float(np.mean([a.elapsed_time(b) for a, b in ev_step]))
+        value = rows / (ms_per_step * 1e-3)
 
     n_active = int(layer.ws_view(abi.WS_NACTIVE, c.T, 4).view(torch.int32).item())
     work = algorithmic_work(c, n_active)
@@ -454,7 +472,8 @@ def main():
         cpu = cpu_baseline(c, idx_d.cpu().numpy(), w_d.cpu().numpy())
 
     line = {
-        "metric": "routed rows/sec (TxK) for the MoE prefill layer",
+        "metric": "routed rows/sec (TxK) for the MoE prefill layer"
+                  + (", cold cache" if flush is not None else ""),
         "value": round(value, 1),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -470,7 +489,9 @@ def main():
                                + (", D4 activations" if c.wtype == synth.Q8_0_D4 else ""),
                    "T": c.T, "H": c.H,
                    "F": c.F, "E": c.E, "K": c.K, "wtype": synth.WTYPE_NAME[c.wtype],
-                   "group_size": 16, "active_experts": n_active, "stage_events": use_events},
+                   "group_size": 16, "active_experts": n_active, "stage_events": use_events,
+                   **({"cache": f"cold: {args.cold_mib} MiB written between steps, each step "
+                                "timed by events around it"} if flush is not None else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
