@@ -27,9 +27,9 @@
 //     hold one block of 32 features;
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
 // K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of LDS
-// buffers with direct global->LDS loads (global_load_lds_dwordx4), three stages ahead of the
-// MFMAs for Q4_1 (a ring of four) and two for Q8_0 (a ring of three), so the registers hold no
-// staged data and no VALU moves it.  The weights come
+// buffers with direct global->LDS loads (global_load_lds_dwordx4), one stage ahead of the
+// MFMAs for Q4_1 (a ring of two, three workgroups per CU) and two for Q8_0 (a ring of three,
+// two workgroups per CU), so the registers hold no staged data and no VALU moves it.  The weights come
 // from the group buffer's MMQ layout (64-row tiles of one stage, each contiguous, every row's
 // block headers first), so a workgroup's weight stage is two contiguous runs, and in LDS the
 // rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart.  q8_1 rows keep their 144-byte groups.  LDS
@@ -82,11 +82,17 @@ struct alignas(16) StageBuf {
   uint8_t b[kRowsN * Geo<WT>::kBRow];
 };
 
-// LDS stage buffers per workgroup: four for Q4_1 (19.5 KB each: two workgroups per CU still fit,
-// and three stages are in flight ahead of the MFMAs), three for Q8_0 (26.6 KB each).
+// LDS stage buffers per workgroup and workgroups per CU.  Q4_1: two buffers (19.5 KB each, one
+// stage in flight ahead of the MFMAs) so that three workgroups fit in a CU's 160 KB and the
+// kernel's 164 VGPRs: three wavefronts per SIMD hide each other's waits better than deeper
+// prefetch does (a ring of four at two workgroups per CU was 6-8% slower).  Q8_0: three
+// buffers (26.6 KB each, two stages ahead) at two workgroups per CU (at three its registers
+// spill).  The raw block-dot epilogue and the per-group kernel stay at two workgroups per CU
+// (they would spill at three).
 template <int WT>
 struct Ring {
-  static constexpr int kN = WT == 1 ? 4 : 3;
+  static constexpr int kN = WT == 1 ? 2 : 3;
+  static constexpr int kWgPerCu = WT == 1 ? 3 : 2;
   StageBuf<WT> buf[kN];
 };
 
@@ -218,7 +224,7 @@ __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
 
 template <int WT, int EPI>
 __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, StageBuf<WT>& L2,
-                                         StageBuf<WT>& L3, const MmqProblem& p, const uint8_t* W, int row0,
+                                         const MmqProblem& p, const uint8_t* W, int row0,
                                          int nrows, int ntile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -249,10 +255,6 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   }
   const v16i izero = {0};
   const v16f fzero = {0.0f};
-  // f16 operand of dx_b for block b: fp16 slot 2b (Q4_1) or b (Q8_0), every other slot zero
-  v4i za[kKB];
-#pragma unroll
-  for (int b = 0; b < kKB; ++b) za[b] = (v4i){0, 0, 0, 0};
 
   auto issue = [&](StageBuf<WT>& buf, int t) {
     issue_stage<WT>(buf, plan, abase + (size_t)t * kARow, W + (size_t)t * 64 * Geo<WT>::kBRow);
@@ -268,9 +270,7 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   auto step = [&](int s, const StageBuf<WT>& cur, StageBuf<WT>& fill) {
     // (the raw block-dot epilogue also stores inside the loop, so it drains the counter)
     const int ahead = EPI == 2 ? 0 : min(Ring<WT>::kN - 2, nstages - 1 - s);
-    if (ahead >= 2)
-      __builtin_amdgcn_s_waitcnt(vm_imm(2 * kMinDmaPerStage<WT>));
-    else if (ahead == 1)
+    if (ahead == 1)
       __builtin_amdgcn_s_waitcnt(vm_imm(kMinDmaPerStage<WT>));
     else
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
@@ -322,18 +322,20 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
       // 2 * dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero).  D4's fp32
       // dx_b goes in as two fp16 (hi = fp16(dx), lo = fp16(dx - hi)) in slots 2b, 2b+1, both
       // facing dw_b: the MFMA adds hi*dw + lo*dw, each product exact in fp32
+      // f16 operand of dx_b: fp16 slot 2b (Q4_1, D4) or b (Q8_0), every other slot zero
+      v4i za = {0, 0, 0, 0};
       if (WT == 1) {
-        za[b][b] = (int)((uint32_t)hx[b] & 0xffffu);
+        za[b] = (int)((uint32_t)hx[b] & 0xffffu);
       } else if (WT == kWtQ8_0D4) {
         const float dx = __int_as_float(hx[b]);
         const _Float16 hi = (_Float16)dx;
         const _Float16 lo = (_Float16)(dx - (float)hi);
-        za[b][b] = (int)((uint32_t)__builtin_bit_cast(uint16_t, hi) |
+        za[b] = (int)((uint32_t)__builtin_bit_cast(uint16_t, hi) |
                          ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
       } else {
-        za[b][b >> 1] = (b & 1) ? (int)((uint32_t)hx[b] << 16) : (int)((uint32_t)hx[b] & 0xffffu);
+        za[b >> 1] = (b & 1) ? (int)((uint32_t)hx[b] << 16) : (int)((uint32_t)hx[b] & 0xffffu);
       }
-      const v8h sx = __builtin_bit_cast(v8h, za[b]);
+      const v8h sx = __builtin_bit_cast(v8h, za);
       const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
       const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw1, fzero, 0, 0, 0);
 #pragma unroll
@@ -356,16 +358,13 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the previous tile
   __builtin_amdgcn_s_barrier();        // ... and every other wave's, before the ring refills
   issue(L0, 0);
-  if (nstages > 1) issue(L1, 1);
-  if (Ring<WT>::kN == 4) {
-    if (nstages > 2) issue(L2, 2);
-    for (int s0 = 0; s0 < nstages; s0 += 4) {
-      step(s0, L0, L3);
+  if (Ring<WT>::kN == 2) {  // stage s + 1 goes into the other buffer once s is complete
+    for (int s0 = 0; s0 < nstages; s0 += 2) {
+      step(s0, L0, L1);
       if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
-      if (s0 + 2 < nstages) step(s0 + 2, L2, L1);
-      if (s0 + 3 < nstages) step(s0 + 3, L3, L2);
     }
   } else {
+    if (nstages > 1) issue(L1, 1);
     for (int s0 = 0; s0 < nstages; s0 += 3) {
       step(s0, L0, L2);
       if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
@@ -461,7 +460,7 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
 constexpr int kXcds = 8;
 
 template <int WT, int EPI>
-__global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
+__global__ __launch_bounds__(256, EPI == 2 ? 2 : Ring<WT>::kWgPerCu) void mmq_layer_kernel(MmqProblem p) {
   __shared__ Ring<WT> ring;
   const int ntl = gridDim.x;
   const int live = ntl * (p.tile_count > 0 ? p.tile_count : *p.n_tiles);
@@ -479,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void mmq_layer_kernel(MmqProblem p) {
                                          ? p.wbase + p.w_off[t.expert]
                                          : p.wbase + (size_t)t.ordinal * p.pos_stride);
   if (((uintptr_t)W & 15) != 0) return;  // the direct-to-LDS loads need 16-byte alignment
-  mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[2], ring.buf[Ring<WT>::kN - 1], p, W,
+  mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W,
                     t.row0, t.nrows, work % ntl);
 }
 
@@ -491,7 +490,7 @@ __global__ __launch_bounds__(256, 2) void mmq_group_kernel(MmqProblem p) {
   const int r0 = p.offsets[e], cnt = p.offsets[e + 1] - r0;
   const uint8_t* W = p.wbase + (size_t)j * p.pos_stride + p.mat_offset;
   for (int m = blockIdx.y; m * kRowsM < cnt; m += gridDim.y)
-    mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[2], ring.buf[Ring<WT>::kN - 1], p, W,
+    mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W,
                       r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM), blockIdx.x);
 }
 
