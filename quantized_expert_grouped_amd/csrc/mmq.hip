@@ -28,8 +28,8 @@
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
 // K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of LDS
 // buffers with direct global->LDS loads (global_load_lds_dwordx4), one stage ahead of the
-// MFMAs for Q4_1 (a ring of two, three workgroups per CU) and two for Q8_0 (a ring of three,
-// two workgroups per CU), so the registers hold no staged data and no VALU moves it.  The weights come
+// MFMAs (a ring of two, three workgroups per CU; with D4 activations two stages ahead, a ring
+// of three, two workgroups per CU), so the registers hold no staged data and no VALU moves it.  The weights come
 // from the group buffer's MMQ layout (64-row tiles of one stage, each contiguous, every row's
 // block headers first), so a workgroup's weight stage is two contiguous runs, and in LDS the
 // rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart.  q8_1 rows keep their 144-byte groups.  LDS
@@ -82,17 +82,17 @@ struct alignas(16) StageBuf {
   uint8_t b[kRowsN * Geo<WT>::kBRow];
 };
 
-// LDS stage buffers per workgroup and workgroups per CU.  Q4_1: two buffers (19.5 KB each, one
-// stage in flight ahead of the MFMAs) so that three workgroups fit in a CU's 160 KB and the
-// kernel's 164 VGPRs: three wavefronts per SIMD hide each other's waits better than deeper
-// prefetch does (a ring of four at two workgroups per CU was 6-8% slower).  Q8_0: three
-// buffers (26.6 KB each, two stages ahead) at two workgroups per CU (at three its registers
-// spill).  The raw block-dot epilogue and the per-group kernel stay at two workgroups per CU
-// (they would spill at three).
+// LDS stage buffers per workgroup and workgroups per CU.  Q4_1 and Q8_0: two buffers (19.5 or
+// 26.6 KB each, one stage in flight ahead of the MFMAs) so that three workgroups fit in a CU's
+// 160 KB and in 168 VGPRs: three wavefronts per SIMD hide each other's waits better than deeper
+// prefetch does (a ring of four, or three, at two workgroups per CU was 5-9% slower).  Q8_0
+// with D4 activations: three buffers (two stages ahead) at two workgroups per CU (at three its
+// registers spill).  The raw block-dot epilogue and the per-group kernel stay at two
+// workgroups per CU (they would spill at three).
 template <int WT>
 struct Ring {
-  static constexpr int kN = WT == 1 ? 2 : 3;
-  static constexpr int kWgPerCu = WT == 1 ? 3 : 2;
+  static constexpr int kN = WT == kWtQ8_0D4 ? 3 : 2;
+  static constexpr int kWgPerCu = WT == kWtQ8_0D4 ? 2 : 3;
   StageBuf<WT> buf[kN];
 };
 
@@ -306,13 +306,17 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
     const v4i hx = *reinterpret_cast<const v4i*>(arow);
     const v8h hw0 = __builtin_bit_cast(v8h, b_header<WT>(brow0));
     const v8h hw1 = __builtin_bit_cast(v8h, b_header<WT>(brow1));
-    // the LDS reads of each block's operands are issued one block ahead of its MFMAs
+    // Q4_1: the LDS reads of each block's operands are issued one block ahead of its MFMAs
     v4i fa = a_frag<WT>(arow, 0, half), f0 = b_raw<WT>(brow0, 0, half),
         f1 = b_raw<WT>(brow1, 0, half);
 #pragma unroll
     for (int b = 0; b < kKB; ++b) {
-      const v4i a = fa, x0 = f0, x1 = f1;
-      if (b + 1 < kKB) {
+      // Q8_0 reads each block's operands where it uses them: its 4-VGPR weight fragments held
+      // one block ahead would not fit three workgroups' registers
+      const v4i a = WT == 1 ? fa : a_frag<WT>(arow, b, half);
+      const v4i x0 = WT == 1 ? f0 : b_raw<WT>(brow0, b, half);
+      const v4i x1 = WT == 1 ? f1 : b_raw<WT>(brow1, b, half);
+      if (WT == 1 && b + 1 < kKB) {
         fa = a_frag<WT>(arow, b + 1, half);
         f0 = b_raw<WT>(brow0, b + 1, half);
         f1 = b_raw<WT>(brow1, b + 1, half);
