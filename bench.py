@@ -49,6 +49,7 @@ WORKLOAD_DOC = {
     "t8k": "T=8192 H=2048 F=512 E=512 K=10 Q4_1, uniform routing",
     "t32k": "T=32768 H=2048 F=512 E=512 K=10 Q8_0, uniform routing",
     "t30k_zipf": "T=30118 H=2048 F=512 E=512 K=10 Q4_1, Zipf-skewed routing",
+    "t30k_z092": "T=30118 H=2048 F=512 E=512 K=10 Q4_1, Zipf-skewed routing, exponent 0.92",
 }
 
 

@@ -1,4 +1,4 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark times.
+"""GPU parity at the named workloads' full sizes, in the launch configuration the benchmark times.
 
 The oracle cannot run whole layers of this size in seconds, so it checks what it can compute
 one by one: routing, maps and quantised rows in full or on samples, and the output rows of
@@ -14,7 +14,7 @@ from quantized_expert_grouped_amd.layer import MoePrefillLayer
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-@pytest.mark.parametrize("name", ["tiny", "t2k", "t8k", "t32k", "t30k_zipf", "t2k_d4"])
+@pytest.mark.parametrize("name", ["tiny", "t2k", "t8k", "t32k", "t30k_zipf", "t30k_z092", "t2k_d4"])
 def test_full_size_workload(orc, name):
     if name.endswith("_d4"):                 # the same Q8_0 experts with D4 activations
         c = synth.config_case(name[:-3])
