@@ -222,7 +222,7 @@ __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
   return (v4i){(int)d.x, (int)d.y, 0, 0};
 }
 
-template <int WT, int EPI>
+template <int WT, int EPI, int NG = 4>
 __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, StageBuf<WT>& L2,
                                          const MmqProblem& p, const uint8_t* W, int row0,
                                          int nrows, int ntile) {
@@ -343,7 +343,7 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
       const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
       const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw1, fzero, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 4 * NG; ++i) {  // registers 4g..4g+3 hold rows 8g..8g+7
         acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
         acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
       }
@@ -482,8 +482,22 @@ __global__ __launch_bounds__(256, EPI == 2 ? 2 : Ring<WT>::kWgPerCu) void mmq_la
                                          ? p.wbase + p.w_off[t.expert]
                                          : p.wbase + (size_t)t.ordinal * p.pos_stride);
   if (((uintptr_t)W & 15) != 0) return;  // the direct-to-LDS loads need 16-byte alignment
-  mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W,
-                    t.row0, t.nrows, work % ntl);
+  // the wavefront's live 8-row groups: an expert's last tile skips the epilogue of its
+  // padding rows (the MFMAs still cover all 32)
+  const int nh = t.nrows - 32 * (wave_id() >> 1);
+  const int ng = (EPI == 2 || nh <= 0 || nh >= 32) ? 4 : (nh + 7) / 8;
+  if (ng == 4)
+    mmq_tile<WT, EPI, 4>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+                         t.nrows, work % ntl);
+  else if (ng == 3)
+    mmq_tile<WT, EPI, 3>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+                         t.nrows, work % ntl);
+  else if (ng == 2)
+    mmq_tile<WT, EPI, 2>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+                         t.nrows, work % ntl);
+  else
+    mmq_tile<WT, EPI, 1>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+                         t.nrows, work % ntl);
 }
 
 template <int WT, int EPI>
