@@ -22,7 +22,7 @@ namespace {
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
-constexpr int kGatherThreads = 256;
+constexpr int kGatherThreads = 512;
 constexpr int kGatherUnroll = 4;
 
 __device__ __forceinline__ void copy_span(const uint8_t* __restrict__ src,
