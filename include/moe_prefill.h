@@ -95,6 +95,9 @@ const char *moe_strerror(int status);
 size_t moe_block_bytes(int wtype);                      /* 34 or 20; 0 if unknown */
 size_t moe_expert_bytes(int H, int F, int wtype);       /* 3*H*F/32 blocks */
 size_t moe_q8_1_row_bytes(int n);                       /* n/128*144 */
+/* The two workspace queries return 0 for shapes the matching entry point would refuse
+ * (non-positive sizes, T*K above 2^30, H or F not a positive multiple of 128, unknown type,
+ * group_size outside 1..MOE_MAX_GROUP). */
 size_t moe_build_maps_workspace_size(int T, int K, int E);
 size_t moe_workspace_size(int T, int H, int F, int E, int K, int wtype, int group_size);
 

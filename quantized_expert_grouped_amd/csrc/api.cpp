@@ -56,7 +56,7 @@ size_t moe_expert_bytes(int H, int F, int wtype) {
 size_t moe_q8_1_row_bytes(int n) { return n > 0 ? (size_t)(n / 128) * 144 : 0; }
 
 size_t moe_build_maps_workspace_size(int T, int K, int E) {
-  if (T < 1 || K < 1 || E < 1) return 0;
+  if (T < 1 || K < 1 || E < 1 || (long long)T * K > (1LL << 30)) return 0;
   return align_up((size_t)map_chunks(T * K) * E * 4, 256);
 }
 

@@ -27,8 +27,11 @@ struct Layout {
 };
 
 inline bool make_layout(int T, int H, int F, int E, int K, int wt, Layout* L) {
-  if (T < 1 || K < 1 || E < 1 || H < 128 || F < 128 || !valid_wtype(wt)) return false;
+  if (T < 1 || K < 1 || E < 1 || H < 128 || H % 128 != 0 || F < 128 || F % 128 != 0 ||
+      !valid_wtype(wt))
+    return false;
   const size_t R = (size_t)T * K;
+  if (R > ((size_t)1 << 30)) return false;  // the row indices are int32
   const size_t eb = moe_expert_bytes(H, F, wt);
   size_t o = 0;
   auto take = [&](size_t bytes) {

@@ -55,7 +55,11 @@ def test_version_and_sizes():
     # at least q8 rows of x and h, Dm, and one group position per expert
     assert ws >= R * 2304 + R * 576 + R * 2048 * 4 + 512 * 1966080
     assert abi.workspace_size(8192, 2048, 512, 512, 10, abi.Q4_1, 17) == 0
-    assert abi.workspace_size(8192, 2000, 512, 512, 10, abi.Q4_1, 16) == 0 or True
+    assert abi.workspace_size(8192, 2000, 512, 512, 10, abi.Q4_1, 16) == 0     # H % 128
+    assert abi.workspace_size(8192, 2048, 500, 512, 10, abi.Q4_1, 16) == 0     # F % 128
+    assert abi.workspace_size(1 << 27, 2048, 512, 512, 10, abi.Q4_1, 16) == 0  # T*K > 2^30
+    assert abi.build_maps_workspace_size(1 << 27, 10, 512) == 0
+    assert abi.build_maps_workspace_size(8192, 10, 512) > 0
     offs = [abi.workspace_offset(i, 100, 256, 128, 16, 2, abi.Q8_0) for i in range(10)]
     assert all(o % 256 == 0 for o in offs)
     assert abi.workspace_offset(abi.WS_GROUP_STRIDE, 100, 256, 128, 16, 2, abi.Q8_0) % 256 == 0
