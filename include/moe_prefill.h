@@ -103,7 +103,8 @@ size_t moe_workspace_size(int T, int H, int F, int E, int K, int wtype, int grou
 
 /* a0  Top-K routing ([QS] "Identity": routing built as Prefill builds it, 10 of 512 experts).
  * logits fp32 [T x E] -> idx int32 [T x K] (the K largest logits, equal logits: lower id first),
- * w fp32 [T x K] (softmax over the K chosen logits = softmax, top-K, renormalise).  E <= 2048. */
+ * w fp32 [T x K] (softmax over the K chosen logits = softmax, top-K, renormalise).  E <= 2048.
+ * The logits must be finite (the kernel marks picked entries -inf). */
 int moe_route_topk(const float *logits, int T, int E, int K, int32_t *idx, float *w,
                    void *stream);
 

@@ -4,9 +4,10 @@
 // them with the softmax of those K logits.
 //
 // One wavefront per token: lane l holds logits l, l+64, ... in registers (coalesced loads); K
-// rounds of a wave-wide (value desc, id asc) argmax pick the experts (DPP steps inside each row of
-// 16 lanes, then the 4 rows' winners read into scalars: no LDS round trip on the chain); lane k
-// keeps pick k and the weights come from one wave-wide sum.  (value desc, id asc) is a strict
+// rounds of a wave-wide (value desc, id asc) argmax pick the experts (a branch-free lane-local
+// pass, DPP steps inside each row of 16 lanes, then the 4 rows' winners read into scalars: no LDS
+// round trip on the chain); the pick is set to -inf in its lane; lane k keeps pick k and the
+// weights come from one wave-wide sum.  (value desc, id asc) is a strict
 // order on distinct ids, so the winner does not depend on the order of the comparisons.
 #include <math.h>
 
@@ -47,26 +48,28 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wavefront
   const float* l = logits + (size_t)t * E;
+  // lane l holds logits l, l+64, ...; ids past E and picked entries read -inf (the logits are
+  // finite, so such an entry never wins while K <= E)
   float v[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int id = j * 64 + lane;
-    v[j] = id < E ? l[id] : 0.0f;
+    v[j] = id < E ? l[id] : -INFINITY;
   }
-  uint32_t taken = 0;
   float my_v = 0.0f;
   int my_id = 0;
   for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int bid = 0x7fffffff;
+    // the lane's best: its ids grow with j, so only a strictly larger value displaces the best
+    // so far (equal values keep the lower id), with no branch per entry
+    float bv = v[0];
+    int bj = 0;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int id = j * 64 + lane;
-      if (id < E && !((taken >> j) & 1u) && better(v[j], id, bv, bid)) {
-        bv = v[j];
-        bid = id;
-      }
+    for (int j = 1; j < VPL; ++j) {
+      const bool gt = v[j] > bv;
+      bv = gt ? v[j] : bv;
+      bj = gt ? j : bj;
     }
+    int bid = bj * 64 + lane;
     // best within each row of 16 lanes (every lane of the row ends with it), then of the 4 rows
     dpp_best<kDppXor1>(bv, bid);
     dpp_best<kDppXor2>(bv, bid);
@@ -87,7 +90,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
       bv = rv;
       bid = rid;
     }
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+    // the pick leaves its lane's candidates (pj, pl uniform)
+    const int pj = bid >> 6, pl = bid & 63;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) v[j] = (j == pj && lane == pl) ? -INFINITY : v[j];
     if (lane == k) {
       my_v = bv;
       my_id = bid;
