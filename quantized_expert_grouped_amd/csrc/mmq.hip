@@ -26,10 +26,9 @@
 //     h = silu(g) * u is formed in registers and requantised along F across the 32 lanes that
 //     hold one block of 32 features;
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
-// K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of LDS
+// K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of two LDS
 // buffers with direct global->LDS loads (global_load_lds_dwordx4), one stage ahead of the
-// MFMAs (a ring of two, three workgroups per CU; with D4 activations two stages ahead, a ring
-// of three, two workgroups per CU), so the registers hold no staged data and no VALU moves it.  The weights come
+// MFMAs, at three workgroups per CU, so the registers hold no staged data and no VALU moves it.  The weights come
 // from the group buffer's MMQ layout (64-row tiles of one stage, each contiguous, every row's
 // block headers first), so a workgroup's weight stage is two contiguous runs, and in LDS the
 // rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart.  q8_1 rows keep their 144-byte groups.  LDS
@@ -82,18 +81,16 @@ struct alignas(16) StageBuf {
   uint8_t b[kRowsN * Geo<WT>::kBRow];
 };
 
-// LDS stage buffers per workgroup and workgroups per CU.  Q4_1 and Q8_0: two buffers (19.5 or
-// 26.6 KB each, one stage in flight ahead of the MFMAs) so that three workgroups fit in a CU's
-// 160 KB and in 168 VGPRs: three wavefronts per SIMD hide each other's waits better than deeper
-// prefetch does (a ring of four, or three, at two workgroups per CU was 5-9% slower).  Q8_0
-// with D4 activations: three buffers (two stages ahead) at two workgroups per CU (at three its
-// registers spill).  The raw block-dot epilogue and the per-group kernel stay at two
-// workgroups per CU (they would spill at three).
+// LDS stage buffers per workgroup: two (19.5 KB for Q4_1, 26.6 KB for Q8_0; one stage in flight
+// ahead of the MFMAs), so that three workgroups fit in a CU's 160 KB and in 168 VGPRs: three
+// wavefronts per SIMD hide each other's waits better than deeper prefetch does (a ring of four,
+// or three, at two workgroups per CU was 5-9% slower).  The raw block-dot epilogue and the
+// per-group kernel stay at two workgroups per CU (they would spill at three).
+constexpr int kWgPerCu = 3;
+
 template <int WT>
 struct Ring {
-  static constexpr int kN = WT == kWtQ8_0D4 ? 3 : 2;
-  static constexpr int kWgPerCu = WT == kWtQ8_0D4 ? 2 : 3;
-  StageBuf<WT> buf[kN];
+  StageBuf<WT> buf[2];
 };
 
 // s_waitcnt immediate for vmcnt(n) (0 <= n < 64) with the other counters left alone
@@ -130,13 +127,6 @@ __device__ __forceinline__ void plan_dma(DmaPlan<WT>& d, size_t act_row_bytes, i
     d.b[j] = (uint32_t)(c < k ? tile0 + 16 * c : tile1 + 16 * (c - k));
   }
 }
-
-// DMA instructions issued per stage by the wavefront that issues the fewest (wavefront w issues
-// instructions w, w+4, ... of each operand).  Waiting until at most this many loads are in
-// flight completes the current stage on every wavefront; a wavefront that issues more also waits
-// for its first extra loads of the next stage, which only shortens its lookahead.
-template <int WT>
-constexpr int kMinDmaPerStage = kAInstr / 4 + Geo<WT>::kBInstr / 4;
 
 // One direct global->LDS load: lane i's 16 (or 4) bytes land at lds + 16*i (4*i), lds
 // wave-uniform (it is passed in M0).  Written as inline assembly so that the compiler's wait-count
@@ -223,7 +213,7 @@ __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
 }
 
 template <int WT, int EPI, int NG = 4>
-__device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, StageBuf<WT>& L2,
+__device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
                                          const MmqProblem& p, const uint8_t* W, int row0,
                                          int nrows, int ntile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -261,21 +251,15 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   };
 
 
-  // One stage: wait until stage s is in LDS for every wave (which also means every wave is done
-  // with stage s-1, whose buffer `fill` then receives stage s + ring - 1), then its MFMAs.  The
-  // ring's buffers are distinct LDS objects used with fixed roles per unrolled step, so the
-  // compiler can tell the reads of one from the loads into another and keeps the loads in flight.
-  // With ahead = the stages already issued after s, waiting until at most ahead * kMin loads
-  // are outstanding completes stage s on every wavefront (loads retire in issue order).
+  // One stage: wait until this wavefront's loads of stage s are done and, at the barrier, every
+  // wavefront's (which also means every wavefront is done with stage s-1, whose buffer `fill`
+  // then receives stage s + 1), then its MFMAs.  The two buffers are distinct LDS objects used
+  // with fixed roles per unrolled step, so the compiler can tell the reads of one from the
+  // loads into the other and keeps the loads in flight.
   auto step = [&](int s, const StageBuf<WT>& cur, StageBuf<WT>& fill) {
-    // (the raw block-dot epilogue also stores inside the loop, so it drains the counter)
-    const int ahead = EPI == 2 ? 0 : min(Ring<WT>::kN - 2, nstages - 1 - s);
-    if (ahead == 1)
-      __builtin_amdgcn_s_waitcnt(vm_imm(kMinDmaPerStage<WT>));
-    else
-      __builtin_amdgcn_s_waitcnt(vm_imm(0));
+    __builtin_amdgcn_s_waitcnt(vm_imm(0));
     __builtin_amdgcn_s_barrier();
-    if (s + Ring<WT>::kN - 1 < nstages) issue(fill, s + Ring<WT>::kN - 1);
+    if (s + 1 < nstages) issue(fill, s + 1);
     if (!live) return;
     const uint8_t* arow = cur.a + (32 * wr + l32) * kARow;
     const uint8_t* brow0 = cur.b + (32 * ct0 + l32) * Geo<WT>::kBRow;
@@ -368,18 +352,9 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the previous tile
   __builtin_amdgcn_s_barrier();        // ... and every other wave's, before the ring refills
   issue(L0, 0);
-  if (Ring<WT>::kN == 2) {  // stage s + 1 goes into the other buffer once s is complete
-    for (int s0 = 0; s0 < nstages; s0 += 2) {
-      step(s0, L0, L1);
-      if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
-    }
-  } else {
-    if (nstages > 1) issue(L1, 1);
-    for (int s0 = 0; s0 < nstages; s0 += 3) {
-      step(s0, L0, L2);
-      if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
-      if (s0 + 2 < nstages) step(s0 + 2, L2, L1);
-    }
+  for (int s0 = 0; s0 < nstages; s0 += 2) {  // stage s + 1 goes into the other buffer
+    step(s0, L0, L1);
+    if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
   }
   if (EPI == 2) return;
   if (EPI == 1) {  // every wavefront is past its last stage: the ring becomes scratch
@@ -470,7 +445,7 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1, Sta
 constexpr int kXcds = 8;
 
 template <int WT, int EPI>
-__global__ __launch_bounds__(256, EPI == 2 ? 2 : Ring<WT>::kWgPerCu) void mmq_layer_kernel(MmqProblem p) {
+__global__ __launch_bounds__(256, EPI == 2 ? 2 : kWgPerCu) void mmq_layer_kernel(MmqProblem p) {
   __shared__ Ring<WT> ring;
   const int ntl = gridDim.x;
   const int live = ntl * (p.tile_count > 0 ? p.tile_count : *p.n_tiles);
@@ -493,16 +468,16 @@ __global__ __launch_bounds__(256, EPI == 2 ? 2 : Ring<WT>::kWgPerCu) void mmq_la
   const int nh = t.nrows - 32 * (wave_id() >> 1);
   const int ng = (EPI == 2 || nh <= 0 || nh >= 32) ? 4 : (nh + 7) / 8;
   if (ng == 4)
-    mmq_tile<WT, EPI, 4>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+    mmq_tile<WT, EPI, 4>(ring.buf[0], ring.buf[1], p, W, t.row0,
                          t.nrows, work % ntl);
   else if (ng == 3)
-    mmq_tile<WT, EPI, 3>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+    mmq_tile<WT, EPI, 3>(ring.buf[0], ring.buf[1], p, W, t.row0,
                          t.nrows, work % ntl);
   else if (ng == 2)
-    mmq_tile<WT, EPI, 2>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+    mmq_tile<WT, EPI, 2>(ring.buf[0], ring.buf[1], p, W, t.row0,
                          t.nrows, work % ntl);
   else
-    mmq_tile<WT, EPI, 1>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W, t.row0,
+    mmq_tile<WT, EPI, 1>(ring.buf[0], ring.buf[1], p, W, t.row0,
                          t.nrows, work % ntl);
 }
 
@@ -514,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void mmq_group_kernel(MmqProblem p) {
   const int r0 = p.offsets[e], cnt = p.offsets[e + 1] - r0;
   const uint8_t* W = p.wbase + (size_t)j * p.pos_stride + p.mat_offset;
   for (int m = blockIdx.y; m * kRowsM < cnt; m += gridDim.y)
-    mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], ring.buf[Ring<WT>::kN - 1], p, W,
+    mmq_tile<WT, EPI>(ring.buf[0], ring.buf[1], p, W,
                       r0 + m * kRowsM, min(kRowsM, cnt - m * kRowsM), blockIdx.x);
 }
 
