@@ -131,10 +131,24 @@ def copy_probe(mib: int, dev) -> None:
     del src, dst
 
 
-def cpu_baseline(c, idx, w, target_s: float = 12.0):
-    """Time the oracle (as it stands) on the first tokens of the same workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(c, idx, w, target_s: float = 12.0, threads: int = 0):
+    """Time the oracle (as it stands) on the first tokens of the same workload, on all the
+    host threads OpenMP gives it or on ``threads`` of them."""
     import oracle
     oracle.lib()
+    if threads > 0:
+        oracle.set_threads(threads)
     threads = oracle.get_threads()
     # size the sample from a short probe so that the measured run takes ~target_s
     probe_t = 16
@@ -151,7 +165,7 @@ def cpu_baseline(c, idx, w, target_s: float = 12.0):
     return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_tok} tokens of {c.name} ({rows} routed rows): the whole oracle "
                       f"layer (maps, q8_1 scatter, every routed row through its expert, combine) "
-                      f"in {dt:.2f} s on {threads} threads"}
+                      f"in {dt:.2f} s on {threads} threads of {cpu_model()}"}
 
 
 PEAK_PCIE_GBS = 64.0           # PCIe 5.0 x16, one direction, GB/s
@@ -328,6 +342,8 @@ def main():
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the steps without the per-stage events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads for the CPU baseline (default: all OpenMP gives)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the steps (counter "
                          "calibration; outside the timed region)")
@@ -470,7 +486,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         idx_d, w_d = layer.route(logits)
-        cpu = cpu_baseline(c, idx_d.cpu().numpy(), w_d.cpu().numpy())
+        cpu = cpu_baseline(c, idx_d.cpu().numpy(), w_d.cpu().numpy(), threads=args.cpu_threads)
 
     line = {
         "metric": "routed rows/sec (TxK) for the MoE prefill layer"
