@@ -50,7 +50,8 @@ def _d4_scale_bound(wtype, wmat, n_out, k_in, act, dots):
 
 
 @pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
-@pytest.mark.parametrize("shape", [(150, 512, 256, 12, 3, None), (700, 256, 128, 16, 2, 1.5)])
+@pytest.mark.parametrize("shape", [(150, 512, 256, 12, 3, None), (700, 256, 128, 16, 2, 1.5),
+                                   (90, 384, 384, 10, 3, None)])      # three stages each
 def test_mmq_block_dots_bit_exact(orc, wtype, shape):
     T, H, F, E, K, skew = shape
     c, m, q8x, experts, gbuf = _setup(orc, wtype, T, H, F, E, K, seed=T + wtype, skew=skew)
@@ -76,7 +77,8 @@ def test_mmq_block_dots_bit_exact(orc, wtype, shape):
 
 
 @pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_1, synth.Q8_0_D4])
-@pytest.mark.parametrize("shape", [(150, 512, 256, 12, 3, None), (1300, 256, 128, 4, 1, 3.0)])
+@pytest.mark.parametrize("shape", [(150, 512, 256, 12, 3, None), (1300, 256, 128, 4, 1, 3.0),
+                                   (90, 384, 384, 10, 3, None)])
 def test_mmq_down_f32(orc, wtype, shape):
     """The down projection's fp32 rows (n_out = H, k_in = F) on random q8_1 rows of h."""
     T, H, F, E, K, skew = shape
