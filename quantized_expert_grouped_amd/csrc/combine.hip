@@ -1,6 +1,7 @@
 // a7  Combine.  "#1282 prefill: STRATA_PREFILL_CPU_SHARE=auto hands a small chunk's least-routed
 // experts to the idle CPU pool", "What it does": the expert output rows in Dm are unweighted and
-// the combine applies the routing weights to them.  out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i],
+// the combine applies the routing weights to them.
+//   out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i],
 // k ascending (fp32 fused multiply-adds in that fixed order, so the result depends only on the
 // token's own rows).
 //

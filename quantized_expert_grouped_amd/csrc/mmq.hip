@@ -28,18 +28,17 @@
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
 // K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of two LDS
 // buffers with direct global->LDS loads (global_load_lds_dwordx4), one stage ahead of the
-// MFMAs, at three workgroups per CU, so the registers hold no staged data and no VALU moves it.  The weights come
-// from the group buffer's MMQ layout (64-row tiles of one stage, each contiguous, every row's
-// block headers first), so a workgroup's weight stage is two contiguous runs, and in LDS the
-// rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart.  q8_1 rows keep their 144-byte groups.  LDS
-// serves 8-byte reads 32 lanes and 16-byte reads 16 lanes at a time over 64 four-byte banks:
-// the 16-byte reads at both strides and Q8_0's 8-byte pairs are conflict-free; Q4_1's 8-byte
-// weight reads conflict 2-way (reading two blocks' halves with one 16-byte read instead
-// measured no faster).  A lane half h
-// takes elements 16h..16h+15 of a block on both operands: one 16-byte activation read (an
-// 8-byte pair 16 bytes apart would conflict 2-way on the 144-byte row stride) and, for Q4_1,
-// the block's 8-byte half h, whose low and high nibbles the gather arranged to be exactly
-// those elements, split with two masks.
+// MFMAs, at three workgroups per CU, so the registers hold no staged data and no VALU moves it.
+// The weights come from the group buffer's MMQ layout (64-row tiles of one stage, each
+// contiguous, every row's block headers first), so a workgroup's weight stage is two contiguous
+// runs, and in LDS the rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart.  q8_1 rows keep their
+// 144-byte groups.  LDS serves 8-byte reads 32 lanes and 16-byte reads 16 lanes at a time over
+// 64 four-byte banks: the 16-byte reads at both strides and Q8_0's 8-byte pairs are
+// conflict-free; Q4_1's 8-byte weight reads conflict 2-way (reading two blocks' halves with one
+// 16-byte read instead measured no faster).  A lane half h takes elements 16h..16h+15 of a block
+// on both operands: one 16-byte activation read (an 8-byte pair 16 bytes apart would conflict
+// 2-way on the 144-byte row stride) and, for Q4_1, the block's 8-byte half h, whose low and
+// high nibbles the gather arranged to be exactly those elements, split with two masks.
 #include <math.h>
 
 #include "common.hpp"
@@ -250,7 +249,6 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
     issue_stage<WT>(buf, plan, abase + (size_t)t * kARow, W + (size_t)t * 64 * Geo<WT>::kBRow);
   };
 
-
   // One stage: wait until this wavefront's loads of stage s are done and, at the barrier, every
   // wavefront's (which also means every wavefront is done with stage s-1, whose buffer `fill`
   // then receives stage s + 1), then its MFMAs.  The two buffers are distinct LDS objects used
@@ -427,7 +425,9 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
         make_uint4(qw[0], qw[1], qw[2], qw[3]);
     if (part == 0) {
       const uint32_t hdr =
-          !nz ? 0u : WT == kWtQ8_0D4 ? __float_as_uint(d) : (f2h(d) | (q8_1_scale_bits(d, S) << 16));
+          !nz                ? 0u
+          : WT == kWtQ8_0D4 ? __float_as_uint(d)
+                            : (f2h(d) | (q8_1_scale_bits(d, S) << 16));
       *reinterpret_cast<uint32_t*>(dst + hoff + (fb & 3) * 4) = hdr;
     }
     if (p.debug_h != nullptr) {
