@@ -12,8 +12,9 @@
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every buffer; the
- *     library allocates nothing on any compute path and keeps no state between calls (the
- *     optional stage profiler aside).
+ *     library allocates nothing on any compute path and keeps no state between calls, apart
+ *     from the optional stage profiler and a streamed walk's own object (moe_walk_create, whose
+ *     ring bookkeeping and events carry from one call to the next by design).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is enqueued on it
  *     and the call returns at once; nothing synchronises with the host.
  *   - Return value: MOE_OK (0) or a negative moe_status.  Argument checks run on the host before
