@@ -254,8 +254,9 @@ typedef struct moe_walk moe_walk;
  * must stay allocated until moe_walk_destroy has returned.  *walk is set on MOE_OK; MOE_EHIP if
  * a HIP resource (or the host memory) could not be made.  A walk serves one call at a time: its
  * host-side plan, read-back buffer and slot map are not guarded, so two threads must not call
- * moe_prefill_layer_streamed on the same walk at once (calls in sequence, on any streams, are
- * ordered by its events). */
+ * moe_prefill_layer_streamed on the same walk at once.  For calls in sequence, even on different
+ * streams, the walk's events order the reuse of its ring slots; a workspace or output shared
+ * between such calls follows the general rule above. */
 int moe_walk_create(void *ring, int n_slots, size_t slot_stride, moe_walk **walk);
 
 /* Waits for the walk's copies and for every gather that read its ring (the slots' events), then
