@@ -19,9 +19,13 @@
  *     and the call returns at once; nothing synchronises with the host.
  *   - Return value: MOE_OK (0) or a negative moe_status.  Argument checks run on the host before
  *     anything is enqueued (MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE); a failed launch returns
- *     MOE_EHIP.  Device-side preconditions (0 <= expert id < E, finite inputs) are the caller's:
- *     the kernels never read or write out of bounds when they are broken, but the results are then
- *     unspecified.
+ *     MOE_EHIP.  Device-side data is not checked on the host.  A routed expert id outside [0, E)
+ *     is a caller error that the kernels detect: the maps give such a route slot = -1 and a row
+ *     past offsets[E] with src = -1, it contributes nothing to the output, and its count is
+ *     stored in device memory (moe_build_maps: the first int32 of ws; the layer: the first of
+ *     the workspace's MOE_WS_STATUS words), 0 when every id is in range; nothing is read or
+ *     written out of bounds.  Finite inputs (x, logits, the experts' scales) are the caller's duty: with
+ *     non-finite ones the results are unspecified, but the kernels stay in bounds.
  *   - Calls are reentrant; calls that share output or workspace buffers must not overlap.
  *
  * Byte formats (little endian)
@@ -57,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 #define MOE_MAX_GROUP 16     /* experts per group buffer ([G1] "What": MMQ_GROUP = 16) */
 #define MOE_MAX_E 2048       /* largest expert count the kernels accept */
 #define MOE_MAX_K 64         /* largest routes per token */
@@ -115,7 +119,10 @@ int moe_route_topk(const float *logits, int T, int E, int K, int32_t *idx, float
  *   by expert id ascending, ascending t*K+k inside an expert (stable); slot [T*K] = src^-1;
  *   order [E]: the experts with rows, in ring order from ring_start ([G2] "What changes": skipped
  *   ring entries hold no rows); n_active [1]: how many.  Group g of size gs is order[gs*g ...].
- * ws: at least moe_build_maps_workspace_size(T, K, E) bytes of device scratch. */
+ * An id outside [0, E) counts as one more expert after the last: its entries take rows
+ * offsets[E] .. T*K-1 (index order) with src = -1, and their slot is -1.
+ * ws: at least moe_build_maps_workspace_size(T, K, E) bytes of device scratch; after the call its
+ * first int32 holds the number of ids outside [0, E). */
 int moe_build_maps(const int32_t *topk_idx, int T, int K, int E, int ring_start,
                    int32_t *counts, int32_t *offsets, int32_t *src, int32_t *slot,
                    int32_t *order, int32_t *n_active, void *ws, size_t ws_bytes, void *stream);
@@ -124,7 +131,8 @@ int moe_build_maps(const int32_t *topk_idx, int T, int K, int E, int ring_start,
  * x fp32 [T x H] row-major; q8 [T*K x moe_q8_1_row_bytes(H)].
  * mode without MOE_QUANT_PER_ROW (scatter): each token row is read once and written to rows
  * slot[t*K+k], k < K.  With it (per-row gather, the form the page replaces): row r quantises
- * token src[r]/K.  Both write the same bytes.  MOE_QUANT_D4: rows in the D4 layout. */
+ * token src[r]/K.  Both write the same bytes.  MOE_QUANT_D4: rows in the D4 layout.  A slot
+ * (scatter) or src (per-row) of -1 writes nothing. */
 int moe_quantize_scatter_q8_1(const float *x, int T, int H, int K, const int32_t *slot,
                               const int32_t *src, int mode, void *q8, void *stream);
 
@@ -168,7 +176,8 @@ int moe_mmq_grouped(int wtype, const void *group_buf, size_t pos_stride, size_t 
 
 /* a7  Combine ([CS] "What it does": Dm holds the expert rows without their routing weights, which
  * the combine applies).
- * out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i], k ascending; Dm fp32 [T*K x H]. */
+ * out[t,i] = sum_{k<K} w[t,k] * Dm[slot[t*K+k], i], k ascending, a route with slot -1 left out;
+ * Dm fp32 [T*K x H]. */
 int moe_combine(const float *Dm, const int32_t *slot, const float *topk_w, int T, int K, int H,
                 float *out, void *stream);
 
@@ -191,9 +200,9 @@ int moe_prefill_layer(const float *x, int T, int H, int F, int E, int K,
  * (the pages' gather exists to assemble a group buffer from expert slots, [G1] "What"; an expert
  * pool that never leaves device memory can be put in the matmul's layout once, with
  * moe_gather_group_mmq, and read in place).  packed_pool: expert e in the MMQ layout at byte
- * expert_off[e] (int64 [E], device; multiples of 16: a tile whose weights are not 16-byte
- * aligned is skipped and its rows are unspecified; inside the pool: the caller's duty, as for
- * moe_prefill_layer).  The matmul sees the bytes moe_prefill_layer gathers, so the output is
+ * expert_off[e] (int64 [E], device; multiples of 16: an expert at an offset that is not is
+ * skipped, its rows are unspecified and the second MOE_WS_STATUS word is set non-zero; inside the
+ * pool: the caller's duty, as for moe_prefill_layer).  The matmul sees the bytes moe_prefill_layer gathers, so the output is
  * that call's with the same arguments, bit for bit; ws as there
  * (moe_workspace_size with any group size; the group region is not used). */
 int moe_prefill_layer_packed(const float *x, int T, int H, int F, int E, int K,
@@ -215,7 +224,11 @@ enum {
     MOE_WS_GROUPS = 7,   /* group buffers: active expert i (ring order) at i * stride */
     MOE_WS_HQ8 = 8,      /* q8_1 rows of h [T*K x moe_q8_1_row_bytes(F)] */
     MOE_WS_DM = 9,       /* fp32 [T*K x H] */
-    MOE_WS_GROUP_STRIDE = 10  /* not an offset: the byte stride between group positions */
+    MOE_WS_GROUP_STRIDE = 10, /* not an offset: the byte stride between group positions */
+    MOE_WS_STATUS = 11        /* int32 [2], rewritten by every layer call: [0] the routed ids
+                                 outside [0, E); [1] non-zero when moe_prefill_layer_packed met an
+                                 expert whose bytes are not 16-byte aligned (its rows are then
+                                 unspecified); 0 and 0 for a clean call */
 };
 size_t moe_workspace_offset(int which, int T, int H, int F, int E, int K, int wtype,
                             int group_size);

@@ -60,13 +60,10 @@ def lib():
             "orc_quantize_gather": (None, [P, i, i, i, P, i, P]),
             "orc_quantize_scatter": (None, [P, i, i, i, P, i, P]),
             "orc_gather": (None, [P, P, P, i, sz, P, i, sz]),
-            "orc_mmq_expert_bytes": (sz, [i, i, i]),
-            "orc_mmq_pack": (None, [i, P, i, i, P]),
-            "orc_gather_mmq": (None, [P, P, P, i, i, i, i, P, i, sz]),
             "orc_block_idot": (ctypes.c_int32, [i, P, P]),
             "orc_row_dot": (ctypes.c_double, [i, P, P, i]),
             "orc_block_dots": (None, [i, P, i, i, P, i, P]),
-            "orc_mmq_rows": (None, [i, P, i, i, P, i, P]),
+            "orc_matrix_rows": (None, [i, P, i, i, P, i, P]),
             "orc_expert_row": (None, [i, P, i, i, P, P, P, P]),
             "orc_combine": (None, [P, P, P, i, i, i, P]),
             "orc_prefill_layer": (i, [P, i, i, i, i, i, P, P, i, P, P, P, P, P, P, P]),
@@ -205,33 +202,6 @@ def gather(pool, expert_off, experts, expert_bytes_: int, group_buf, first_pos: 
     return group_buf
 
 
-def mmq_expert_bytes(H: int, F: int, wtype: int) -> int:
-    """Bytes of one expert in the group buffer's MMQ layout."""
-    return int(lib().orc_mmq_expert_bytes(H, F, wtype))
-
-
-def mmq_pack(wtype: int, expert, H: int, F: int):
-    """One raw expert rewritten in the MMQ layout (groups of 4 blocks, headers first)."""
-    expert = _c(expert, np.uint8)
-    assert expert.size == expert_bytes(H, F, wtype)
-    out = np.empty(mmq_expert_bytes(H, F, wtype), np.uint8)
-    lib().orc_mmq_pack(wtype, _p(expert), H, F, _p(out))
-    return out
-
-
-def gather_mmq(pool, expert_off, experts, wtype: int, H: int, F: int, group_buf, first_pos: int,
-               pos_stride: int):
-    pool = _c(pool, np.uint8)
-    expert_off = _c(expert_off, np.int64)
-    experts = _c(experts, np.int32)
-    assert group_buf.dtype == np.uint8 and group_buf.flags.c_contiguous
-    eb = mmq_expert_bytes(H, F, wtype)
-    assert (first_pos + len(experts) - 1) * pos_stride + eb <= group_buf.size
-    lib().orc_gather_mmq(_p(pool), _p(expert_off), _p(experts), len(experts), wtype, H, F,
-                         _p(group_buf), int(first_pos), int(pos_stride))
-    return group_buf
-
-
 # ---- a4 / a6 -----------------------------------------------------------------------------
 def block_idot(wtype: int, wblock, xq) -> int:
     wblock = _c(wblock, np.uint8)
@@ -254,13 +224,13 @@ def block_dots(wtype: int, wmat, n_out: int, k_in: int, act_q8):
     return out
 
 
-def mmq_rows(wtype: int, wmat, n_out: int, k_in: int, act_q8):
+def matrix_rows(wtype: int, wmat, n_out: int, k_in: int, act_q8):
     """fp64 products [n_rows x n_out] of activation rows with a weight matrix's rows."""
     wmat = _c(wmat, np.uint8)
     act_q8 = _c(act_q8, np.uint8)
     n_rows = act_q8.shape[0]
     out = np.empty((n_rows, n_out), np.float64)
-    lib().orc_mmq_rows(wtype, _p(wmat), n_out, k_in, _p(act_q8), n_rows, _p(out))
+    lib().orc_matrix_rows(wtype, _p(wmat), n_out, k_in, _p(act_q8), n_rows, _p(out))
     return out
 
 

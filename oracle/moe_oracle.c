@@ -284,75 +284,6 @@ void orc_gather(const uint8_t *pool, const int64_t *expert_off, const int32_t *e
 }
 
 /* ---------------------------------------------------------------------------------------
- * a3  gather into the MMQ layout.  The pages copy an expert's bytes unchanged; the layout of
- * the group buffer is free in that nothing reads it but the grouped matmul.  This library's
- * matmul stages its weights as tiles of 64 rows by 128 values (4 blocks, the span of one q8_1
- * group), so its gather writes each tile-stage as one contiguous run, every row's 4 blocks
- * with their headers first:
- *   a matrix of n_rows rows and nblk blocks per row, for tile j < n_rows/64, stage t < nblk/4,
- *   row i < 64 (matrix row 64j+i) holds blocks 4t..4t+3 of that row at byte
- *   ((j*(nblk/4) + t)*64 + i) * G, G = 4 * block bytes, as
- *     Q4_1 (G = 80) : (d, m) of the 4 blocks (16 B), then 16 packed bytes of each block (64 B)
- *                     in the order of two halves: byte 8h + i (h < 2, i < 8) holds element
- *                     16h + i in its low nibble and element 16h + 8 + i in its high nibble
- *                     (the raw block's byte j holds elements j and j + 16), so the elements
- *                     16h..16h+15 of a block sit in one 8-byte half
- *     Q8_0 (G = 136): d of the 4 blocks (8 B), then q[32] of the 4 blocks (128 B)
- * The expert keeps its order gate | up | down and its size.  Positions in the group buffer are
- * as in orc_gather.
- * Pinned in tests/test_oracle_gather_dot.py: decoding the packed bytes by this description
- * gives every block's (d, m, q) of the raw expert.
- * ------------------------------------------------------------------------------------- */
-size_t orc_mmq_expert_bytes(int H, int F, int wtype) { return orc_expert_bytes(H, F, wtype); }
-
-static void mmq_pack_matrix(int wtype, const uint8_t *raw, int n_rows, int nblk, uint8_t *out)
-{
-    size_t bb = orc_block_bytes(wtype), G = 4 * bb;
-    int stages = nblk / 4;
-    for (int n = 0; n < n_rows; ++n)
-        for (int t = 0; t < stages; ++t) {
-            const uint8_t *src = raw + ((size_t)n * nblk + (size_t)4 * t) * bb;
-            uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;
-            for (int j = 0; j < 4; ++j) {
-                if (wtype == ORC_Q4_1) {
-                    const uint8_t *qs = src + j * bb + 4;
-                    uint8_t v[32];                                    /* the block's elements */
-                    for (int e = 0; e < 16; ++e) {
-                        v[e] = qs[e] & 15;
-                        v[e + 16] = qs[e] >> 4;
-                    }
-                    memcpy(dst + 4 * j, src + j * bb, 4);             /* d, m */
-                    for (int h = 0; h < 2; ++h)
-                        for (int i = 0; i < 8; ++i)
-                            dst[16 + 16 * j + 8 * h + i] =
-                                (uint8_t)(v[16 * h + i] | (v[16 * h + 8 + i] << 4));
-                } else {
-                    memcpy(dst + 2 * j, src + j * bb, 2);             /* d */
-                    memcpy(dst + 8 + 32 * j, src + j * bb + 2, 32);   /* q */
-                }
-            }
-        }
-}
-
-void orc_mmq_pack(int wtype, const uint8_t *expert, int H, int F, uint8_t *out)
-{
-    size_t bb = orc_block_bytes(wtype);
-    size_t gu = (size_t)F * (H / 32) * bb;
-    mmq_pack_matrix(wtype, expert, F, H / 32, out);                     /* gate */
-    mmq_pack_matrix(wtype, expert + gu, F, H / 32, out + gu);           /* up */
-    mmq_pack_matrix(wtype, expert + 2 * gu, H, F / 32, out + 2 * gu);   /* down */
-}
-
-void orc_gather_mmq(const uint8_t *pool, const int64_t *expert_off, const int32_t *experts,
-                    int n, int wtype, int H, int F, uint8_t *group_buf, int first_pos,
-                    size_t pos_stride)
-{
-    for (int j = 0; j < n; ++j)
-        orc_mmq_pack(wtype, pool + expert_off[experts[j]], H, F,
-                     group_buf + (size_t)(first_pos + j) * pos_stride);
-}
-
-/* ---------------------------------------------------------------------------------------
  * a4 / a6  block dots (MMQ).  [G2] "What changes" and [QS] opening section: the grouped
  * quantised matmul on q8_1 activations.  For weight block b of row n and activation block b
  * of row r:  I_b = sum_j qw_j * qx_j  (integer),
@@ -425,7 +356,7 @@ void orc_block_dots(int wtype, const uint8_t *wmat, int n_out, int k_in,
 
 /* Products of n_rows activation rows with every row of one weight matrix (fp64):
  * out[r*n_out + n] = orc_row_dot(row n of wmat, activation row r). */
-void orc_mmq_rows(int wtype, const uint8_t *wmat, int n_out, int k_in, const uint8_t *act_q8,
+void orc_matrix_rows(int wtype, const uint8_t *wmat, int n_out, int k_in, const uint8_t *act_q8,
                   int n_rows, double *out)
 {
     size_t wrb = (size_t)(k_in / 32) * orc_block_bytes(wtype), arb = orc_q8_1_row_bytes(k_in);

@@ -78,20 +78,13 @@ void orc_quantize_scatter(const float *x, int T, int H, int K, const int32_t *sl
 /* --- a3 gather ------------------------------------------------------------------------- */
 void orc_gather(const uint8_t *pool, const int64_t *expert_off, const int32_t *experts, int n,
                 size_t expert_bytes, uint8_t *group_buf, int first_pos, size_t pos_stride);
-/* the same positions, each expert written in the MMQ layout (64-row tiles of 4-block stages,
- * each row's block headers first; same size as the raw expert) */
-size_t orc_mmq_expert_bytes(int H, int F, int wtype);
-void orc_mmq_pack(int wtype, const uint8_t *expert, int H, int F, uint8_t *out);
-void orc_gather_mmq(const uint8_t *pool, const int64_t *expert_off, const int32_t *experts,
-                    int n, int wtype, int H, int F, uint8_t *group_buf, int first_pos,
-                    size_t pos_stride);
 
 /* --- a4 / a6 block dots ----------------------------------------------------------------- */
 int32_t orc_block_idot(int wtype, const uint8_t *wblock, const int8_t *xq);
 double  orc_row_dot(int wtype, const uint8_t *wrow, const uint8_t *xrow_q8, int k_in);
 void    orc_block_dots(int wtype, const uint8_t *wmat, int n_out, int k_in,
                        const uint8_t *act_q8, int n_rows, int32_t *out);
-void    orc_mmq_rows(int wtype, const uint8_t *wmat, int n_out, int k_in,
+void    orc_matrix_rows(int wtype, const uint8_t *wmat, int n_out, int k_in,
                      const uint8_t *act_q8, int n_rows, double *out);
 
 /* --- a4..a6 one routed row through one expert ------------------------------------------ */

@@ -19,7 +19,7 @@ Q8_0, Q4_1, Q8_0_D4 = 0, 1, 2
 QUANT_PER_ROW, QUANT_D4 = 1, 2
 EPI_F32, EPI_SWIGLU_Q8_1, EPI_I32_BLOCKDOTS = 0, 1, 2
 WS_COUNTS, WS_OFFSETS, WS_SRC, WS_SLOT, WS_ORDER, WS_NACTIVE, WS_Q8X, WS_GROUPS, WS_HQ8, WS_DM, \
-    WS_GROUP_STRIDE = range(11)
+    WS_GROUP_STRIDE, WS_STATUS = range(12)
 N_STAGES = 6
 STAGES = ("maps", "quantize", "gather", "gate_up", "down", "combine")
 

@@ -57,7 +57,7 @@ size_t moe_q8_1_row_bytes(int n) { return n > 0 ? (size_t)(n / 128) * 144 : 0; }
 
 size_t moe_build_maps_workspace_size(int T, int K, int E) {
   if (T < 1 || K < 1 || E < 1 || (long long)T * K > (1LL << 30)) return 0;
-  return align_up((size_t)map_chunks(T * K) * E * 4, 256);
+  return kMapsHistAt + align_up(maps_hist_bytes(T * K, E), 256);
 }
 
 size_t moe_workspace_size(int T, int H, int F, int E, int K, int wtype, int group_size) {
@@ -84,6 +84,7 @@ size_t moe_workspace_offset(int which, int T, int H, int F, int E, int K, int wt
     case MOE_WS_HQ8: return L.hq8;
     case MOE_WS_DM: return L.dm;
     case MOE_WS_GROUP_STRIDE: return L.group_stride;
+    case MOE_WS_STATUS: return L.status;
     default: return (size_t)-1;
   }
 }
@@ -104,8 +105,10 @@ int moe_build_maps(const int32_t* topk_idx, int T, int K, int E, int ring_start,
   if ((long long)T * K > (1LL << 30)) return MOE_EUNSUPPORTED;
   if (E > MOE_MAX_E) return MOE_EUNSUPPORTED;
   if (ws_bytes < moe_build_maps_workspace_size(T, K, E)) return MOE_EWORKSPACE;
-  MapsOut o{counts, offsets, src, slot, order, n_active, static_cast<int32_t*>(ws),
-            nullptr, nullptr, kMmqRows};
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  MapsOut o{counts, offsets, src, slot, order, n_active,
+            reinterpret_cast<int32_t*>(w + kMapsHistAt), nullptr, nullptr, kMmqRows,
+            reinterpret_cast<int32_t*>(w)};
   return status_of(launch_build_maps(topk_idx, T, K, E, ring_start, o, as_stream(stream)));
 }
 
@@ -206,10 +209,7 @@ int moe_prefill_layer(const float* x, int T, int H, int F, int E, int K, const i
 
   hipStream_t s = as_stream(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
-  MapsOut mo{I32(L.counts), I32(L.offsets), I32(L.src), I32(L.slot), I32(L.order),
-             I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
-             I32(L.ntiles), kMmqRows};
+  MapsOut mo = layer_maps(base, L);
 
   hipEvent_t* ev = nullptr;
   {
@@ -246,6 +246,7 @@ int moe_prefill_layer(const float* x, int T, int H, int F, int E, int K, const i
   gu.tiles = mo.tiles;
   gu.n_tiles = mo.n_tiles;
   gu.max_tiles = L.max_tiles;
+  gu.misaligned = reinterpret_cast<int32_t*>(base + L.status) + 1;
   if ((e = launch_mmq(gu, s)) != hipSuccess) return MOE_EHIP;
   mark(4);
   MmqProblem dn = gu;
@@ -278,10 +279,7 @@ int moe_prefill_layer_packed(const float* x, int T, int H, int F, int E, int K,
 
   hipStream_t s = as_stream(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
-  MapsOut mo{I32(L.counts), I32(L.offsets), I32(L.src), I32(L.slot), I32(L.order),
-             I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
-             I32(L.ntiles), kMmqRows};
+  MapsOut mo = layer_maps(base, L);
   if (launch_build_maps(topk_idx, T, K, E, ring_start, mo, s) != hipSuccess ||
       launch_quantize(x, T, H, K, mo.slot, mo.src, act_mode_bits(wtype), base + L.q8x, s) !=
           hipSuccess)
@@ -299,6 +297,7 @@ int moe_prefill_layer_packed(const float* x, int T, int H, int F, int E, int K,
   gu.tiles = mo.tiles;
   gu.n_tiles = mo.n_tiles;
   gu.max_tiles = L.max_tiles;
+  gu.misaligned = reinterpret_cast<int32_t*>(base + L.status) + 1;
   MmqProblem dn = gu;
   dn.epilogue = MOE_EPI_F32;
   dn.mat_offset = (size_t)2 * F * (H / 32) * moe_block_bytes(wtype);

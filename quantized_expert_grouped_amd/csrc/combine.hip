@@ -5,6 +5,8 @@
 // k ascending (fp32 fused multiply-adds in that fixed order, so the result depends only on the
 // token's own rows).
 //
+// A route with slot = -1 (its expert id was out of range, see the maps) adds nothing.
+//
 // One workgroup per token; each thread owns float4 columns of the row (two at a time), reads the
 // K routed rows with 16-byte loads, up to 16 rows' loads per column in flight before their fused
 // multiply-adds, and writes the output once.
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       v4f d0[kBatchK], d1[kBatchK];
 #pragma unroll
       for (int j = 0; j < kBatchK; ++j) {
-        if (k0 + j < K) {
+        if (k0 + j < K && s_row[k0 + j] >= 0) {
           const v4f* row = reinterpret_cast<const v4f*>(Dm + (size_t)s_row[k0 + j] * H);
           d0[j] = __builtin_nontemporal_load(row + c);
           if (two) d1[j] = __builtin_nontemporal_load(row + c + 256);
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
 #pragma unroll
       for (int j = 0; j < kBatchK; ++j) {
-        if (k0 + j < K) {
+        if (k0 + j < K && s_row[k0 + j] >= 0) {
           const float wk = s_w[k0 + j];
           acc0.x = fmaf(wk, d0[j].x, acc0.x);
           acc0.y = fmaf(wk, d0[j].y, acc0.y);

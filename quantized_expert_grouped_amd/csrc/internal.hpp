@@ -31,11 +31,16 @@ struct MapsOut {
   int32_t* slot;      // [R]
   int32_t* order;     // [E]
   int32_t* n_active;  // [1]
-  int32_t* hist;      // [chunks x E] scratch
+  int32_t* hist;      // [chunks x (E+1)] scratch
   MTile* tiles;       // [max tiles] or nullptr
   int32_t* n_tiles;   // [1] or nullptr
   int tile_rows;      // rows per m-tile
+  int32_t* n_invalid; // [2]: routes whose expert id is outside [0, E); [1] set to 0 (the
+                      // layer's MMQ counts skipped misaligned work there)
 };
+// Scratch of moe_build_maps: the status words in the first 256 bytes, then hist.
+constexpr size_t kMapsHistAt = 256;
+inline size_t maps_hist_bytes(int R, int E) { return (size_t)map_chunks(R) * (E + 1) * 4; }
 hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_start,
                              const MapsOut& o, hipStream_t s);
 inline int max_mtiles(int R, int E, int tile_rows) { return R / tile_rows + (E < R ? E : R); }
@@ -92,12 +97,21 @@ struct MmqProblem {
   const int32_t* n_tiles;
   int max_tiles;
   int tile_count;
+  int n_tiles_n;          // weight-row tiles per m-tile (set by the launcher)
+  int32_t* misaligned;    // layer form, packed pool: count of m-tiles skipped (or nullptr)
   // group form: positions j < n_group hold experts[j], rows from offsets
   const int32_t* offsets;
   int experts[16];
   int n_group;
 };
 hipError_t launch_mmq(const MmqProblem& p, hipStream_t s);
+// The layer's MMQ launch is one-dimensional: n-tiles x m-tiles workgroups must fit in x.
+constexpr long long kMaxGridX = 0x7fffffffLL;
+inline long long mmq_layer_workgroups(int n_out_gu, int n_out_dn, int max_tiles) {
+  const long long a = (long long)(n_out_gu / 64) * max_tiles;    // gate/up: 64 features a tile
+  const long long b = (long long)(n_out_dn / 128) * max_tiles;   // down: 128 output columns
+  return a > b ? a : b;
+}
 
 // ---- a7 combine -----------------------------------------------------------------------------
 hipError_t launch_combine(const float* Dm, const int32_t* slot, const float* w, int T, int K,

@@ -21,7 +21,7 @@ static_assert(MOE_Q8_0_D4 == kWtQ8_0D4 && MOE_QUANT_PER_ROW == kQuantPerRow &&
 
 // Region offsets of the layer's workspace (each 256-byte aligned).
 struct Layout {
-  size_t hist, counts, offsets, src, slot, order, nactive, ntiles, tiles, q8x, groups, hq8, dm;
+  size_t status, hist, counts, offsets, src, slot, order, nactive, ntiles, tiles, q8x, groups, hq8, dm;
   size_t group_stride, total;
   int max_tiles;
 };
@@ -39,7 +39,8 @@ inline bool make_layout(int T, int H, int F, int E, int K, int wt, Layout* L) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L->hist = take((size_t)map_chunks((int)R) * E * 4);
+  L->status = take(8);
+  L->hist = take(maps_hist_bytes((int)R, E));
   L->counts = take((size_t)E * 4);
   L->offsets = take((size_t)(E + 1) * 4);
   L->src = take(R * 4);
@@ -56,6 +57,14 @@ inline bool make_layout(int T, int H, int F, int E, int K, int wt, Layout* L) {
   L->dm = take(R * (size_t)H * 4);
   L->total = o;
   return true;
+}
+
+// The map outputs of the layer, in its workspace at `base`.
+inline MapsOut layer_maps(uint8_t* base, const Layout& L) {
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  return MapsOut{I32(L.counts), I32(L.offsets), I32(L.src), I32(L.slot), I32(L.order),
+                 I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
+                 I32(L.ntiles), kMmqRows, I32(L.status)};
 }
 
 // The layer's argument checks (moe_prefill_layer and its streamed form), in the order the
@@ -75,6 +84,7 @@ inline int check_layer_args(const float* x, int T, int H, int F, int E, int K,
   if (expert_bytes != moe_expert_bytes(H, F, wtype)) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256)) return MOE_EINVAL;
   if (!make_layout(T, H, F, E, K, wtype, L)) return MOE_EINVAL;
+  if (mmq_layer_workgroups(F, H, L->max_tiles) > kMaxGridX) return MOE_EUNSUPPORTED;
   if (ws_bytes < L->total) return MOE_EWORKSPACE;
   return MOE_OK;
 }

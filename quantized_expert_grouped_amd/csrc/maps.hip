@@ -10,8 +10,11 @@
 //   scatter  one wavefront per chunk, 64 entries at a time in index order: ballots over the bits
 //            of the expert id give each lane its equal-id peers, mbcnt its rank among them, so
 //            rows are placed in ascending t*K+k without atomics.
-// Entries with an id outside [0, E) are skipped (a caller error; nothing is accessed out of
-// bounds, the maps are then incomplete).
+// An entry with an id outside [0, E) (a caller error) is counted as one more expert, E, that
+// sorts after every real one: such entries take the rows offsets[E] .. T*K-1, in index order,
+// with src = -1 for those rows and slot = -1 for the entries, so every later step can skip
+// them (the quantiser writes no row for them, the combine adds nothing for them), and the scan
+// stores their number in the status word at the front of the scratch buffer.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -25,11 +28,12 @@ constexpr int kMaxE = 2048;   // largest E the single-workgroup scan holds in LD
 __global__ __launch_bounds__(256) void maps_hist_kernel(const int32_t* __restrict__ idx, int R,
                                                          int E, int nchunks,
                                                          int32_t* __restrict__ hist) {
-  extern __shared__ int32_t lds_hist[];  // [4][E]
+  extern __shared__ int32_t lds_hist[];  // [4][E+1]: bin E counts the out-of-range ids
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int chunk = blockIdx.x * 4 + wave;
-  int32_t* h = lds_hist + wave * E;
-  for (int e = lane; e < E; e += 64) h[e] = 0;
+  const int NB = E + 1;
+  int32_t* h = lds_hist + wave * NB;
+  for (int e = lane; e < NB; e += 64) h[e] = 0;
   __syncthreads();
   if (chunk < nchunks) {
     // every step's ids are loaded before the first is counted: one load latency per chunk
@@ -43,12 +47,12 @@ __global__ __launch_bounds__(256) void maps_hist_kernel(const int32_t* __restric
 #pragma unroll
     for (int it = 0; it < kMapChunk / 64; ++it) {
       const int e = ids[it];
-      if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+      if (base + it * 64 + lane < R) atomicAdd(&h[(unsigned)e < (unsigned)E ? e : E], 1);
     }
   }
   __syncthreads();
   if (chunk < nchunks)
-    for (int e = lane; e < E; e += 64) hist[(size_t)chunk * E + e] = h[e];
+    for (int e = lane; e < NB; e += 64) hist[(size_t)chunk * NB + e] = h[e];
 }
 
 // Exclusive prefix of n ints (n <= 2 * kScanThreads) held as lds[0..n), in place; returns the
@@ -91,7 +95,8 @@ __device__ int block_exclusive_scan(int32_t* lds, int n, int32_t* wave_sums) {
 __global__ __launch_bounds__(kScanThreads) void maps_scan_kernel(
     int E, int nchunks, int ring_start, int32_t* __restrict__ hist, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ order, int32_t* __restrict__ n_active,
-    MTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int tile_rows) {
+    MTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int tile_rows,
+    int32_t* __restrict__ n_invalid) {
   __shared__ int32_t s_cnt[kMaxE];   // rows of expert e
   __shared__ int32_t s_off[kMaxE];   // first row of expert e
   __shared__ int32_t s_act[kMaxE];   // ring position j -> ordinal among the experts with rows
@@ -100,19 +105,26 @@ __global__ __launch_bounds__(kScanThreads) void maps_scan_kernel(
   const int tid = threadIdx.x;
   // per expert: exclusive prefix over chunks (in place), and the count; a batch of chunks'
   // loads is issued before any of them is used, so the chain waits once per batch
+  // (bin E, the out-of-range ids, gets its prefix too: the scatter places them after the rest)
   constexpr int kBatch = 16;
-  for (int e = tid; e < E; e += kScanThreads) {
+  const int NB = E + 1;
+  for (int e = tid; e < NB; e += kScanThreads) {
     int run = 0;
     for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
       int v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        v[u] = c0 + u < nchunks ? hist[(size_t)(c0 + u) * E + e] : 0;
+        v[u] = c0 + u < nchunks ? hist[(size_t)(c0 + u) * NB + e] : 0;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        if (c0 + u < nchunks) hist[(size_t)(c0 + u) * E + e] = run;
+        if (c0 + u < nchunks) hist[(size_t)(c0 + u) * NB + e] = run;
         run += v[u];
       }
+    }
+    if (e == E) {  // the status words: out-of-range ids, and the MMQ's skip count cleared
+      n_invalid[0] = run;
+      n_invalid[1] = 0;
+      continue;
     }
     s_cnt[e] = run;
     s_off[e] = run;
@@ -158,13 +170,14 @@ __global__ __launch_bounds__(256) void maps_scatter_kernel(const int32_t* __rest
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ src,
                                                             int32_t* __restrict__ slot) {
-  extern __shared__ int32_t lds_ctr[];  // [4][E]: each wavefront's next free row per expert
+  extern __shared__ int32_t lds_ctr[];  // [4][E+1]: each wavefront's next free row per expert
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int chunk = blockIdx.x * 4 + wave;
   const bool live = chunk < nchunks;
-  int32_t* ctr = lds_ctr + wave * E;
-  if (live)
-    for (int e = lane; e < E; e += 64) ctr[e] = offsets[e] + hist[(size_t)chunk * E + e];
+  const int NB = E + 1;
+  int32_t* ctr = lds_ctr + wave * NB;
+  if (live)   // offsets[E] = the rows of real experts: bin E's rows follow them
+    for (int e = lane; e < NB; e += 64) ctr[e] = offsets[e] + hist[(size_t)chunk * NB + e];
   __syncthreads();
   if (!live) return;
   // From here each wavefront touches only its own counters; LDS operations of one wavefront
@@ -179,9 +192,10 @@ __global__ __launch_bounds__(256) void maps_scatter_kernel(const int32_t* __rest
 #pragma unroll
   for (int it = 0; it < kMapChunk / 64; ++it) {
     const int i = base + it * 64 + lane;
-    const int e = ids[it];
-    const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t peers = ballot(valid);
+    const bool present = i < R;
+    const bool valid = (unsigned)ids[it] < (unsigned)E;
+    const int e = valid ? ids[it] : E;   // out-of-range ids: bin E (nbits covers it)
+    uint64_t peers = ballot(present);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
       const uint64_t ones = ballot(bit);
@@ -189,10 +203,10 @@ __global__ __launch_bounds__(256) void maps_scatter_kernel(const int32_t* __rest
     }
     const int rank = mbcnt(peers);   // equal-id lanes below this one
     const int cnt = __popcll(peers);
-    if (valid) {
+    if (present) {
       const int r = ctr[e] + rank;
-      src[r] = i;
-      slot[i] = r;
+      src[r] = valid ? i : -1;
+      slot[i] = valid ? r : -1;
       if (rank == 0) ctr[e] = r + cnt;   // after every lane's read above (one instruction stream)
     }
     __builtin_amdgcn_wave_barrier();
@@ -206,13 +220,13 @@ hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_s
   const int R = T * K;
   const int nchunks = map_chunks(R);
   const int blocks = (nchunks + 3) / 4;
-  const size_t lds = (size_t)4 * E * sizeof(int32_t);
+  const size_t lds = (size_t)4 * (E + 1) * sizeof(int32_t);
   maps_hist_kernel<<<blocks, 256, lds, s>>>(idx, R, E, nchunks, o.hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   maps_scan_kernel<<<1, kScanThreads, 0, s>>>(E, nchunks, ring_start, o.hist, o.counts, o.offsets,
                                               o.order, o.n_active, o.tiles, o.n_tiles,
-                                              o.tile_rows);
+                                              o.tile_rows, o.n_invalid);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int nbits = 1;

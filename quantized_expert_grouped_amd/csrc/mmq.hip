@@ -444,25 +444,28 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
 // in one L2, and consecutive m-tiles of an expert share its weights there.
 constexpr int kXcds = 8;
 
+// The launch is one-dimensional (the host keeps n-tiles x m-tiles within the grid's x limit).
 template <int WT, int EPI>
 __global__ __launch_bounds__(256, EPI == 2 ? 2 : kWgPerCu) void mmq_layer_kernel(MmqProblem p) {
   __shared__ Ring<WT> ring;
-  const int ntl = gridDim.x;
+  const int ntl = p.n_tiles_n;
   const int live = ntl * (p.tile_count > 0 ? p.tile_count : *p.n_tiles);
-  const int id = blockIdx.x + ntl * blockIdx.y;
+  const int id = blockIdx.x;
   if (id >= live) return;
-#ifdef MOE_MMQ_NO_XCD_ORDER
-  const int work = id;
-#else
   const int xcd = id % kXcds;
   const int work = xcd * (live / kXcds) + min(xcd, live % kXcds) + id / kXcds;
-#endif
   const int mt = work / ntl;
   const MTile t = p.tiles[mt];
   const uint8_t* W = p.mat_offset + (p.w_off != nullptr
                                          ? p.wbase + p.w_off[t.expert]
                                          : p.wbase + (size_t)t.ordinal * p.pos_stride);
-  if (((uintptr_t)W & 15) != 0) return;  // the direct-to-LDS loads need 16-byte alignment
+  // The direct-to-LDS loads need 16-byte aligned weights.  Group positions always are; a packed
+  // pool's expert offset may not be (a caller error): the tile is then skipped and counted in
+  // the status word the caller can read.
+  if (((uintptr_t)W & 15) != 0) {
+    if (threadIdx.x == 0 && p.misaligned != nullptr) atomicAdd(p.misaligned, 1);
+    return;
+  }
   // the wavefront's live 8-row groups: an expert's last tile skips the epilogue of its
   // padding rows (the MFMAs still cover all 32)
   const int nh = t.nrows - 32 * (wave_id() >> 1);
@@ -497,8 +500,11 @@ template <int WT, int EPI>
 hipError_t launch_typed(const MmqProblem& p, hipStream_t s) {
   const int ntiles = EPI == 1 ? p.n_out / 64 : p.n_out / kRowsN;
   if (p.tiles != nullptr) {
-    const dim3 grid(ntiles, p.tile_count > 0 ? p.tile_count : p.max_tiles);
-    mmq_layer_kernel<WT, EPI><<<grid, 256, 0, s>>>(p);
+    MmqProblem q = p;
+    q.n_tiles_n = ntiles;
+    const long long n = (long long)ntiles * (p.tile_count > 0 ? p.tile_count : p.max_tiles);
+    if (n > kMaxGridX) return hipErrorInvalidConfiguration;   // refused by the ABI's checks
+    mmq_layer_kernel<WT, EPI><<<dim3((unsigned)n), 256, 0, s>>>(q);
   } else {
     const dim3 grid(ntiles, 16, p.n_group);
     mmq_group_kernel<WT, EPI><<<grid, 256, 0, s>>>(p);

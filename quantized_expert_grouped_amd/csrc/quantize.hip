@@ -9,6 +9,9 @@
 // 4 x (d16, s16) then 4 x 32 q.  The D4 layout, which the page names for Q8_0, keeps the 4
 // blocks' fp32 d in the same 16 header bytes instead (the same q, no s).
 //
+// A route whose expert id was out of range has slot = -1 (and its row src = -1, see the maps):
+// nothing is written for it.
+//
 // One wavefront per token (scatter) or per row (per-row form).  A lane owns 16 consecutive
 // values (four coalesced float4 loads), so a block of 32 is a lane pair: one xor-shuffle for
 // amax and one for S.  The chunk's 1152 output bytes (8 groups of 144) are then permuted across
@@ -32,7 +35,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nunits = MODE == 0 ? T : T * K;
   if (unit >= nunits) return;  // uniform per wavefront
-  const int t = MODE == 0 ? unit : src[unit] / K;
+  // a row whose route named no real expert has src = -1 (and its entry slot = -1): no bytes
+  const int sr = MODE == 0 ? 0 : src[unit];
+  if (sr < 0) return;
+  const int t = MODE == 0 ? unit : sr / K;
   const float* xr = x + (size_t)t * H;
   const size_t rb = (size_t)(H / kDs4Vals) * kDs4Bytes;
   int my_row = unit;
@@ -102,6 +108,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     const int npieces = 9 * ngroups;
     for (int k = 0; k < nrows; ++k) {
       const int r = MODE == 0 ? __shfl(my_row, k) : my_row;
+      if (r < 0) continue;  // uniform: a route to no real expert
       uint8_t* seg = q8 + (size_t)r * rb + (size_t)g0 * kDs4Bytes;
       if (lane < npieces) *reinterpret_cast<uint4*>(seg + 16 * lane) = p0;
       if (lane < 8 && 64 + lane < npieces) *reinterpret_cast<uint4*>(seg + 16 * (64 + lane)) = p1;

@@ -227,10 +227,7 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
 
   hipStream_t s = as_stream(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
-  MapsOut mo{I32(L.counts), I32(L.offsets), I32(L.src), I32(L.slot), I32(L.order),
-             I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
-             I32(L.ntiles), kMmqRows};
+  MapsOut mo = layer_maps(base, L);
   auto ok = [](hipError_t e) { return e == hipSuccess; };
 
   // maps, the routing read-back, then the quantiser runs while the host plans the walk
@@ -269,6 +266,7 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
   gu.out = base + L.hq8;
   gu.n_tiles = mo.n_tiles;
   gu.max_tiles = L.max_tiles;
+  gu.misaligned = mo.n_invalid + 1;
   MmqProblem dn = gu;
   dn.epilogue = MOE_EPI_F32;
   dn.mat_offset = (size_t)2 * F * (H / 32) * moe_block_bytes(wtype);

@@ -50,8 +50,10 @@ class MoePrefillLayer:
     def pack_pool(self) -> torch.Tensor:
         """The pool with every expert put in the MMQ layout at its own offset (one gather launch
         per expert; done once, the experts never change), for forward_packed."""
-        packed = torch.zeros_like(self.pool)
         off = self.expert_off.cpu().numpy()
+        if np.any(off % 16 != 0):
+            raise ValueError("the packed layer reads experts at 16-byte aligned offsets only")
+        packed = torch.zeros_like(self.pool)
         base, dst = self.pool.data_ptr(), packed.data_ptr()
         for e in range(self.E):
             o = int(off[e])

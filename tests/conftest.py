@@ -35,3 +35,10 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def oracle_cache():
+    """Whole-workload oracle results computed once per session (the full-size tests of several
+    files compare with the same t8k layer)."""
+    return {}

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert abi.abi_version() == 5
+    assert abi.abi_version() == 6
     assert abi.block_bytes(abi.Q8_0) == 34 and abi.block_bytes(abi.Q4_1) == 20
     assert abi.block_bytes(7) == 0
     assert abi.block_bytes(abi.Q8_0_D4) == 34

@@ -44,6 +44,7 @@ def test_build_maps_bit_exact(orc, T, K, E, ring):
     for key in ("counts", "offsets", "src", "slot", "order"):
         assert np.array_equal(got[key], want[key]), key
     assert got["n_active"] == want["n_active"]
+    assert got["n_invalid"] == 0
 
 
 def test_build_maps_single_expert_skew(orc):
@@ -69,3 +70,51 @@ def test_build_maps_zipf_config(orc):
     for key in ("counts", "offsets", "src", "slot", "order"):
         assert np.array_equal(got[key], want[key]), key
     assert want["n_active"] < E          # some experts receive no rows
+
+
+@pytest.mark.parametrize("T,K,E,ring", [(7, 2, 16, 3), (1000, 10, 512, 123), (4099, 3, 2048, 2047)])
+def test_build_maps_out_of_range_ids(orc, T, K, E, ring):
+    """Ids outside [0, E) (a caller error): they are counted in the scratch's status word, take
+    the rows after every real expert's in index order with src = -1, get slot = -1, and leave
+    the real experts' maps as the oracle gives them with those ids taken as one more expert E
+    (sorting after the rest)."""
+    rng = np.random.default_rng(T + E + 1)
+    idx, _ = orc.route_topk(rng.standard_normal((T, E)).astype(np.float32), K)
+    flat = idx.reshape(-1).copy()
+    bad_at = np.unique(np.concatenate([[0, len(flat) - 1],
+                                       rng.choice(len(flat), max(1, len(flat) // 50))]))
+    bad_vals = np.array([-1, E, E + 7, 2 ** 31 - 1, -(2 ** 31)], np.int64)
+    flat[bad_at] = bad_vals[np.arange(len(bad_at)) % len(bad_vals)].astype(np.int32)
+    bad = flat.reshape(T, K)
+    note(f"maps with {len(bad_at)} out-of-range ids T={T} K={K} E={E}")
+    got, _ = gpu_maps(bad, E, ring)
+    assert got["n_invalid"] == len(bad_at)
+    virt = flat.copy()
+    virt[bad_at] = E                                   # the oracle's view: one more expert
+    want = orc.build_maps(virt.reshape(T, K), E + 1, 0)
+    rv = int(want["offsets"][E])                       # rows of the real experts
+    assert np.array_equal(got["counts"], want["counts"][:E])
+    assert np.array_equal(got["offsets"], want["offsets"][:E + 1])
+    assert np.array_equal(got["src"][:rv], want["src"][:rv])
+    assert np.all(got["src"][rv:] == -1) and len(got["src"]) - rv == len(bad_at)
+    good = np.ones(len(flat), bool)
+    good[bad_at] = False
+    assert np.array_equal(got["slot"][good], want["slot"][good])
+    assert np.all(got["slot"][~good] == -1)
+    order = [(ring + j) % E for j in range(E) if want["counts"][(ring + j) % E] > 0]
+    assert np.array_equal(got["order"], np.array(order, np.int32))
+    # both quantiser forms skip those routes: their rows keep the buffer's old bytes
+    x = rng.standard_normal((T, 256)).astype(np.float32)
+    rb = abi.q8_1_row_bytes(256)
+    for mode in (0, abi.QUANT_PER_ROW):
+        q8 = torch.full((T * K, rb), 0xAB, dtype=torch.uint8, device="cuda")
+        note(f"quantize mode={mode} with out-of-range routes")
+        abi.quantize_scatter_q8_1(dev(x), K, dev(got["slot"]), dev(got["src"]), mode, q8)
+        g = host(q8)
+        assert np.all(g[rv:] == 0xAB)
+        rows = orc.q8_1_rows(x)
+        for i in np.flatnonzero(good)[::max(1, int(good.sum()) // 200)]:
+            assert np.array_equal(g[got["slot"][i]], rows[i // K])
+    # a later call with every id in range clears the count
+    got2, _ = gpu_maps(idx, E, ring)
+    assert got2["n_invalid"] == 0

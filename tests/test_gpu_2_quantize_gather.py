@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 import torch
 
+import mmq_layout
 from gpu_util import dev, empty, gpu_quantize, host, note
 from quantized_expert_grouped_amd import abi, synth
 
@@ -120,8 +121,9 @@ def test_gather_batch_equals_per_expert_launches():
                                                 (synth.Q4_1, 384, 256, 3), (synth.Q8_0, 2048, 512, 0),
                                                 (synth.Q4_1, 2048, 512, 0)])
 def test_gather_group_mmq_bytes(orc, wtype, H, F, misalign):
-    """The MMQ-layout gather against the oracle's, byte for byte: batches of 1..16 at several
-    start positions; sources 8-byte (Q4_1) or 1-byte aligned take the byte-wise path."""
+    """The MMQ-layout gather, decoded, against the oracle's verbatim copy of the raw experts,
+    byte for byte: batches of 1..16 at several start positions, every byte outside the
+    positions untouched; sources 8-byte (Q4_1) or 1-byte aligned take the byte-wise path."""
     rng = np.random.default_rng(H + F + misalign + 10 * wtype)
     eb = abi.expert_bytes(H, F, wtype)
     E = 18
@@ -139,9 +141,10 @@ def test_gather_group_mmq_bytes(orc, wtype, H, F, misalign):
         buf.fill_(0xAB)
         abi.gather_group_mmq([base + int(off[e]) for e in experts], wtype, H, F, buf, first, stride)
         got = host(buf)
-        want = np.full(16 * stride, 0xAB, np.uint8)
-        orc.gather_mmq(pool, off, experts, wtype, H, F, want, first, stride)
-        assert np.array_equal(got, want), (n, first)
+        raw = np.zeros(n * eb, np.uint8)
+        orc.gather(pool, off, experts, eb, raw, 0, eb)
+        mmq_layout.check_positions(got, wtype, H, F, [raw[j * eb:(j + 1) * eb] for j in range(n)],
+                                   first, stride, fill=0xAB)
 
 
 def test_gather_mmq_batch_equals_per_expert_launches():

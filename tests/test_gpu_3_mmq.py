@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import npref
-from gpu_util import dev, empty, host, note
+from gpu_util import dev, empty, gpu_group_buffer, host, note
 from quantized_expert_grouped_amd import abi, synth
 
 pytestmark = pytest.mark.gpu
@@ -20,11 +20,10 @@ def _setup(orc, wtype, T, H, F, E, K, seed, skew=None):
     idx, _ = orc.route_topk(c.logits, K)
     m = orc.build_maps(idx, E)
     q8x = orc.quantize_scatter(c.x, K, m["slot"], orc.act_layout(wtype))
-    # group buffer: positions 0..n-1 hold experts in a shuffled order, in the MMQ layout
+    # group buffer: positions 0..n-1 hold experts in a shuffled order, in the MMQ layout, as the
+    # library's gather writes it (checked against the oracle's copy of the raw experts)
     experts = np.random.default_rng(seed).permutation(E)[:min(E, 16)].astype(np.int32)
-    stride = c.expert_stride
-    gbuf = np.zeros(len(experts) * stride, np.uint8)
-    orc.gather_mmq(c.pool, c.expert_off, experts, wtype, H, F, gbuf, 0, stride)
+    gbuf = gpu_group_buffer(orc, c, experts)
     return c, m, q8x, experts, gbuf
 
 
@@ -58,7 +57,7 @@ def test_mmq_block_dots_bit_exact(orc, wtype, shape):
     R = T * K
     out = torch.zeros((R, 2 * F, H // 32), dtype=torch.int32, device="cuda")
     note(f"mmq i32 wtype={wtype} shape={shape}")
-    abi.mmq_grouped(wtype, dev(gbuf), c.expert_stride, 0, 2 * F, H, experts, dev(m["offsets"]),
+    abi.mmq_grouped(wtype, gbuf, c.expert_stride, 0, 2 * F, H, experts, dev(m["offsets"]),
                     E, dev(q8x), abi.EPI_I32_BLOCKDOTS, out)
     got = host(out)
     gu = 2 * F * (H // 32) * synth.BLOCK_BYTES[wtype]
@@ -89,7 +88,7 @@ def test_mmq_down_f32(orc, wtype, shape):
     mat_off = 2 * F * (H // 32) * synth.BLOCK_BYTES[wtype]
     out = torch.zeros((R, H), dtype=torch.float32, device="cuda")
     note(f"mmq f32 wtype={wtype} shape={shape}")
-    abi.mmq_grouped(wtype, dev(gbuf), c.expert_stride, mat_off, H, F, experts, dev(m["offsets"]),
+    abi.mmq_grouped(wtype, gbuf, c.expert_stride, mat_off, H, F, experts, dev(m["offsets"]),
                     E, dev(hq8), abi.EPI_F32, out)
     got = host(out)
     nb = F // 32
@@ -98,7 +97,7 @@ def test_mmq_down_f32(orc, wtype, shape):
         if r1 == r0:
             continue
         wmat = c.expert(e)[mat_off:mat_off + H * nb * synth.BLOCK_BYTES[wtype]]
-        want = orc.mmq_rows(wtype, wmat, H, F, hq8[r0:r1])
+        want = orc.matrix_rows(wtype, wmat, H, F, hq8[r0:r1])
         dots = orc.block_dots(wtype, wmat, H, F, hq8[r0:r1])
         bound = _abs_term_bound(wtype, wmat, H, F, hq8[r0:r1], dots) * (nb + 2) * 2.0 ** -23
         bound = bound + _d4_scale_bound(wtype, wmat, H, F, hq8[r0:r1], dots)
@@ -113,7 +112,7 @@ def test_mmq_swiglu_q8_1(orc, wtype):
     hq = torch.zeros((R, abi.q8_1_row_bytes(F)), dtype=torch.uint8, device="cuda")
     dh = torch.zeros((R, F), dtype=torch.float32, device="cuda")
     note(f"mmq swiglu wtype={wtype}")
-    abi.mmq_grouped(wtype, dev(gbuf), c.expert_stride, 0, F, H, experts, dev(m["offsets"]), E,
+    abi.mmq_grouped(wtype, gbuf, c.expert_stride, 0, F, H, experts, dev(m["offsets"]), E,
                     dev(q8x), abi.EPI_SWIGLU_Q8_1, hq, dh)
     got_hq, got_h = host(hq), host(dh)
     gu_bytes = F * (H // 32) * synth.BLOCK_BYTES[wtype]
@@ -122,8 +121,8 @@ def test_mmq_swiglu_q8_1(orc, wtype):
         r0, r1 = m["offsets"][e], m["offsets"][e + 1]
         if r1 == r0:
             continue
-        g = orc.mmq_rows(wtype, c.expert(e)[:gu_bytes], F, H, q8x[r0:r1])
-        u = orc.mmq_rows(wtype, c.expert(e)[gu_bytes:2 * gu_bytes], F, H, q8x[r0:r1])
+        g = orc.matrix_rows(wtype, c.expert(e)[:gu_bytes], F, H, q8x[r0:r1])
+        u = orc.matrix_rows(wtype, c.expert(e)[gu_bytes:2 * gu_bytes], F, H, q8x[r0:r1])
         h = g / (1.0 + np.exp(-g)) * u
         # the kernel's h: fp32 accumulation of the same products
         assert np.max(np.abs(got_h[r0:r1] - h)) <= 1e-5 * max(np.max(np.abs(h)), 1e-30)
@@ -143,11 +142,10 @@ def test_mmq_group_position_independence(orc):
     for perm_seed in (0, 1):
         perm = np.random.default_rng(perm_seed).permutation(len(experts))
         ex2 = experts[perm]
-        gb2 = np.zeros_like(gbuf)
-        orc.gather_mmq(c.pool, c.expert_off, ex2, wtype, H, F, gb2, 0, c.expert_stride)
+        gb2 = gpu_group_buffer(orc, c, ex2)
         out = torch.zeros((R, abi.q8_1_row_bytes(F)), dtype=torch.uint8, device="cuda")
         note(f"mmq position permutation {perm_seed}")
-        abi.mmq_grouped(wtype, dev(gb2), c.expert_stride, 0, F, H, ex2, dev(m["offsets"]), E,
+        abi.mmq_grouped(wtype, gb2, c.expert_stride, 0, F, H, ex2, dev(m["offsets"]), E,
                         dev(q8x), abi.EPI_SWIGLU_Q8_1, out)
         outs.append(host(out))
     assert np.array_equal(outs[0], outs[1])
@@ -169,7 +167,7 @@ def test_mmq_down_subnormal_scales(orc, wtype):
     mat_off = 2 * F * (H // 32) * synth.BLOCK_BYTES[wtype]
     out = torch.zeros((R, H), dtype=torch.float32, device="cuda")
     note(f"mmq f32 subnormal scales wtype={wtype}")
-    abi.mmq_grouped(wtype, dev(gbuf), c.expert_stride, mat_off, H, F, experts, dev(m["offsets"]),
+    abi.mmq_grouped(wtype, gbuf, c.expert_stride, mat_off, H, F, experts, dev(m["offsets"]),
                     E, dev(hq8), abi.EPI_F32, out)
     got = host(out)
     nb = F // 32
@@ -178,7 +176,7 @@ def test_mmq_down_subnormal_scales(orc, wtype):
         if r1 == r0:
             continue
         wmat = c.expert(e)[mat_off:mat_off + H * nb * synth.BLOCK_BYTES[wtype]]
-        want = orc.mmq_rows(wtype, wmat, H, F, hq8[r0:r1])
+        want = orc.matrix_rows(wtype, wmat, H, F, hq8[r0:r1])
         dots = orc.block_dots(wtype, wmat, H, F, hq8[r0:r1])
         bound = _abs_term_bound(wtype, wmat, H, F, hq8[r0:r1], dots) * (nb + 2) * 2.0 ** -23
         assert np.all(np.abs(got[r0:r1] - want) <= bound + 1e-38), (j, e)

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import mmq_layout
 from gpu_util import dev, host, note, rel_err
 from quantized_expert_grouped_amd import abi, synth
 from quantized_expert_grouped_amd.layer import MoePrefillLayer
@@ -72,9 +73,11 @@ def test_layer_against_oracle(orc, case):
     assert np.array_equal(region(abi.WS_Q8X, R * xrb).reshape(R, xrb), dbg["q8x"])
     stride = abi.workspace_offset(abi.WS_GROUP_STRIDE, T, H, F, E, K, wtype, 16)
     groups = region(abi.WS_GROUPS, n * stride).reshape(n, stride)
-    for i, e in enumerate(m["order"]):
-        want = orc.mmq_pack(c.wtype, c.expert(e), c.H, c.F)
-        assert np.array_equal(groups[i, :c.expert_bytes], want), (i, e)
+    raw = np.zeros(n * c.expert_bytes, np.uint8)      # the oracle's copy of each position
+    orc.gather(c.pool, c.expert_off, m["order"], c.expert_bytes, raw, 0, c.expert_bytes)
+    mmq_layout.check_positions(groups, c.wtype, c.H, c.F,
+                               [raw[i * c.expert_bytes:(i + 1) * c.expert_bytes]
+                                for i in range(n)], 0, stride)
     Dm = region(abi.WS_DM, R * H * 4).view(np.float32).reshape(R, H)
     assert rel_err(Dm, dbg["Dm"]) <= TOL
 
@@ -153,24 +156,27 @@ def test_layer_repeat_is_deterministic(orc):
 @pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[4], CASES[6]],
                          ids=["tiny", "ragged_q4_1", "skew", "ragged_d4"])
 def test_layer_packed_pool_equals_gathered_layer(orc, case):
-    """Experts kept in the MMQ layout and read in place (no gather): the same bytes reach the
-    matmul, so the output is the gathered layer's bit for bit."""
+    """Experts kept in the MMQ layout and read in place (no gather): the packed pool decodes to
+    the raw pool, the same bytes reach the matmul, so the output is the gathered layer's bit for
+    bit, and within the layer's tolerance of the oracle."""
     name, T, H, F, E, K, wtype, zipf = case
     c = synth.make_case(name, T=T, H=H, F=F, E=E, K=K, wtype=wtype,
                         seed=zlib.crc32(name.encode()) % 10000, zero_tokens=(T // 3,), zipf=zipf)
     idx, w = orc.route_topk(c.logits, K)
+    want = orc.prefill_layer(c.x, idx, w, wtype, c.pool, c.expert_off, F, E)
     layer = _layer(c)
     ref = _run(layer, c, idx, w)
     packed = layer.pack_pool()
-    # the packed pool is the oracle's MMQ layout of every expert
+    # every expert of the packed pool decodes to its raw bytes
     ph = host(packed)
     for e in range(E):
         o = int(c.expert_off[e])
-        assert np.array_equal(ph[o:o + c.expert_bytes], orc.mmq_pack(wtype, c.expert(e), H, F)), e
+        mmq_layout.check_positions(ph[o:o + c.expert_bytes], wtype, H, F, [c.expert(e)], 0, 0)
     note(f"packed layer {name}")
     for rs in (c.ring_start, 0):
         got = host(layer.forward_packed(dev(c.x), dev(idx), dev(w), ring_start=rs))
         assert np.array_equal(got, ref), rs
+        assert rel_err(got, want) <= TOL
 
 
 def test_layer_step_in_a_hip_graph(orc):
@@ -203,3 +209,67 @@ def test_layer_step_in_a_hip_graph(orc):
     idx, w = orc.route_topk(c.logits, c.K)
     assert rel_err(want, orc.prefill_layer(c.x, idx, w, c.wtype, c.pool, c.expert_off, c.F,
                                            c.E)) <= TOL
+
+
+def test_layer_out_of_range_ids_contribute_nothing(orc):
+    """Routes naming no real expert (ids -1, E, E + 7): the layer counts them in its workspace's
+    status word, every other token's row equals the oracle's for the original routing, and a
+    token with such a route equals the oracle with that route's weight set to 0."""
+    c = synth.make_case("badids", T=301, H=512, F=256, E=24, K=4, wtype=synth.Q4_1, seed=17,
+                        zero_tokens=(9,))
+    idx, w = orc.route_topk(c.logits, c.K)
+    rng = np.random.default_rng(4)
+    bad_t = rng.choice(c.T, 20, replace=False)
+    bad = idx.copy()
+    bad_k = rng.integers(0, c.K, len(bad_t))
+    bad[bad_t, bad_k] = np.array([-1, c.E, c.E + 7])[np.arange(len(bad_t)) % 3]
+    bad[bad_t[0], :] = -1                               # one token with no real expert at all
+    layer = _layer(c)
+    got = _run(layer, c, bad, w)
+    n_bad = int(np.sum((bad < 0) | (bad >= c.E)))
+    assert int(host(layer.ws_view(abi.WS_STATUS, c.T, 4)).view(np.int32)[0]) == n_bad
+    want = orc.prefill_layer(c.x, idx, w, c.wtype, c.pool, c.expert_off, c.F, c.E)
+    ok = np.ones(c.T, bool)
+    ok[bad_t] = False
+    assert rel_err(got[ok], want[ok]) <= TOL
+    fixed_i, fixed_w = bad.copy(), w.copy()
+    inval = (bad < 0) | (bad >= c.E)
+    fixed_i[inval], fixed_w[inval] = 0, 0.0
+    want2 = orc.prefill_layer(c.x, fixed_i, fixed_w, c.wtype, c.pool, c.expert_off, c.F, c.E)
+    assert rel_err(got, want2) <= TOL
+    assert not got[bad_t[0]].any()                      # no real route: an exact zero row
+    # the next call with every id in range clears the count and is unaffected
+    got3 = _run(layer, c, idx, w)
+    assert int(host(layer.ws_view(abi.WS_STATUS, c.T, 4)).view(np.int32)[0]) == 0
+    assert rel_err(got3, want) <= TOL
+
+
+def test_packed_layer_flags_a_misaligned_expert(orc):
+    """A packed pool whose expert sits at an offset that is not a multiple of 16 (a caller
+    error, refused by pack_pool): the layer skips that expert's tiles, sets the second status
+    word, and every token not routed to it equals the oracle."""
+    c = synth.make_case("misal", T=200, H=256, F=128, E=12, K=2, wtype=synth.Q4_1, seed=23)
+    idx, w = orc.route_topk(c.logits, c.K)
+    layer = _layer(c)
+    layer.pack_pool()
+    bad_e = int(idx[0, 0])
+    off = c.expert_off.copy()
+    shifted = torch.zeros(layer.pool.numel() + c.expert_bytes + 64, dtype=torch.uint8,
+                          device="cuda")
+    shifted[:layer.packed.numel()] = layer.packed
+    o = int(off[bad_e])
+    tail = layer.pool.numel() + 8                      # the expert's packed bytes, moved to +8
+    shifted[tail:tail + c.expert_bytes] = layer.packed[o:o + c.expert_bytes]
+    off[bad_e] = tail
+    layer.packed = shifted
+    layer.expert_off = dev(off)
+    note("packed layer with one expert at a misaligned offset")
+    got = host(layer.forward_packed(dev(c.x), dev(idx), dev(w)))
+    st = host(layer.ws_view(abi.WS_STATUS, c.T, 8)).view(np.int32)
+    assert st[0] == 0 and st[1] > 0
+    want = orc.prefill_layer(c.x, idx, w, c.wtype, c.pool, c.expert_off, c.F, c.E)
+    ok = ~np.any(idx == bad_e, axis=1)
+    assert ok.sum() > 0 and rel_err(got[ok], want[ok]) <= TOL
+    with pytest.raises(ValueError):
+        layer.expert_off = dev(off)
+        layer.pack_pool()

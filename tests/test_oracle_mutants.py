@@ -42,20 +42,8 @@ MUTANTS = {
                                  "for (int k = 0; k < K; ++k) w[(size_t)t * K + k] = (float)(ex[k] / (sum + 1.0));"),
     "gather_position_ignores_first": ("memcpy(group_buf + (size_t)(first_pos + j) * pos_stride,",
                                       "memcpy(group_buf + (size_t)j * pos_stride,"),
-    "gather_mmq_position_ignores_first": ("group_buf + (size_t)(first_pos + j) * pos_stride);",
-                                          "group_buf + (size_t)j * pos_stride);"),
     "down_at_up_offset": ("const uint8_t *down = expert + (size_t)2 * F * gu_row;",
                           "const uint8_t *down = expert + (size_t)F * gu_row;"),
-    "mmq_pack_q_shifted": ("const uint8_t *qs = src + j * bb + 4;",
-                           "const uint8_t *qs = src + j * bb + 3;"),
-    "mmq_pack_half_nibbles_swapped": ("(uint8_t)(v[16 * h + i] | (v[16 * h + 8 + i] << 4));",
-                                      "(uint8_t)(v[16 * h + 8 + i] | (v[16 * h + i] << 4));"),
-    "mmq_pack_d_order": ("memcpy(dst + 2 * j, src + j * bb, 2);             /* d */",
-                         "memcpy(dst + 6 - 2 * j, src + j * bb, 2);         /* d */"),
-    "mmq_pack_tile_rows": ("uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;",
-                           "uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 32) * G;"),
-    "mmq_pack_row_major": ("uint8_t *dst = out + (((size_t)(n / 64) * stages + t) * 64 + n % 64) * G;",
-                           "uint8_t *dst = out + ((size_t)n * stages + t) * G;"),
     "scatter_first_row_only": ("        for (int k = 1; k < K; ++k)\n            memcpy(q8 + (size_t)slot[(size_t)t * K + k] * rb, row, rb);",
                                "        for (int k = 1; k < 1; ++k)\n            memcpy(q8 + (size_t)slot[(size_t)t * K + k] * rb, row, rb);"),
     "combine_unweighted": ("acc += (double)w[(size_t)t * K + k] * Dm[(size_t)slot[(size_t)t * K + k] * H + i];",
@@ -87,8 +75,6 @@ def _pins(orc):
     yield lambda: tr.test_maps_against_brute_force(orc, 64, 4, 32, 31)
     yield lambda: tg.test_gather_is_per_expert_copy(orc)
     for w in W:
-        yield lambda w=w: tg.test_mmq_pack_keeps_every_block(orc, w, 256, 128)
-        yield lambda w=w: tg.test_gather_mmq_positions(orc, w)
         yield lambda w=w: tg.test_block_idot_against_unpacked_integers(orc, w)
         yield lambda w=w: tg.test_row_dot_against_dequantised_fp64(orc, w)
         yield lambda w=w: tl.test_dense_special_case(orc, w)
