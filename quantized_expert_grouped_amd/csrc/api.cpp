@@ -108,7 +108,7 @@ int moe_build_maps(const int32_t* topk_idx, int T, int K, int E, int ring_start,
   uint8_t* w = static_cast<uint8_t*>(ws);
   MapsOut o{counts, offsets, src, slot, order, n_active,
             reinterpret_cast<int32_t*>(w + kMapsHistAt), nullptr, nullptr, kMmqRows,
-            reinterpret_cast<int32_t*>(w)};
+            reinterpret_cast<int32_t*>(w), nullptr};
   return status_of(launch_build_maps(topk_idx, T, K, E, ring_start, o, as_stream(stream)));
 }
 

@@ -35,8 +35,8 @@ struct MapsOut {
   MTile* tiles;       // [max tiles] or nullptr
   int32_t* n_tiles;   // [1] or nullptr
   int tile_rows;      // rows per m-tile
-  int32_t* n_invalid; // [2]: routes whose expert id is outside [0, E); [1] set to 0 (the
-                      // layer's MMQ counts skipped misaligned work there)
+  int32_t* n_invalid; // [1]: routes whose expert id is outside [0, E)
+  int32_t* mmq_skips; // [1] or nullptr: set to 0 (the layer's MMQ then counts skipped work)
 };
 // Scratch of moe_build_maps: the status words in the first 256 bytes, then hist.
 constexpr size_t kMapsHistAt = 256;

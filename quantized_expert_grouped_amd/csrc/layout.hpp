@@ -64,7 +64,7 @@ inline MapsOut layer_maps(uint8_t* base, const Layout& L) {
   auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
   return MapsOut{I32(L.counts), I32(L.offsets), I32(L.src), I32(L.slot), I32(L.order),
                  I32(L.nactive), I32(L.hist), reinterpret_cast<MTile*>(base + L.tiles),
-                 I32(L.ntiles), kMmqRows, I32(L.status)};
+                 I32(L.ntiles), kMmqRows, I32(L.status), I32(L.status) + 1};
 }
 
 // The layer's argument checks (moe_prefill_layer and its streamed form), in the order the

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kScanThreads) void maps_scan_kernel(
     int E, int nchunks, int ring_start, int32_t* __restrict__ hist, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ order, int32_t* __restrict__ n_active,
     MTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int tile_rows,
-    int32_t* __restrict__ n_invalid) {
+    int32_t* __restrict__ n_invalid, int32_t* __restrict__ mmq_skips) {
   __shared__ int32_t s_cnt[kMaxE];   // rows of expert e
   __shared__ int32_t s_off[kMaxE];   // first row of expert e
   __shared__ int32_t s_act[kMaxE];   // ring position j -> ordinal among the experts with rows
@@ -122,8 +122,8 @@ __global__ __launch_bounds__(kScanThreads) void maps_scan_kernel(
       }
     }
     if (e == E) {  // the status words: out-of-range ids, and the MMQ's skip count cleared
-      n_invalid[0] = run;
-      n_invalid[1] = 0;
+      *n_invalid = run;
+      if (mmq_skips != nullptr) *mmq_skips = 0;
       continue;
     }
     s_cnt[e] = run;
@@ -226,7 +226,7 @@ hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_s
   if (err != hipSuccess) return err;
   maps_scan_kernel<<<1, kScanThreads, 0, s>>>(E, nchunks, ring_start, o.hist, o.counts, o.offsets,
                                               o.order, o.n_active, o.tiles, o.n_tiles,
-                                              o.tile_rows, o.n_invalid);
+                                              o.tile_rows, o.n_invalid, o.mmq_skips);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int nbits = 1;

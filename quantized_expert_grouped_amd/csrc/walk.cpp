@@ -266,7 +266,7 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
   gu.out = base + L.hq8;
   gu.n_tiles = mo.n_tiles;
   gu.max_tiles = L.max_tiles;
-  gu.misaligned = mo.n_invalid + 1;
+  gu.misaligned = mo.mmq_skips;
   MmqProblem dn = gu;
   dn.epilogue = MOE_EPI_F32;
   dn.mat_offset = (size_t)2 * F * (H / 32) * moe_block_bytes(wtype);
