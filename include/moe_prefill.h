@@ -127,6 +127,21 @@ int moe_build_maps(const int32_t *topk_idx, int T, int K, int E, int ring_start,
                    int32_t *counts, int32_t *offsets, int32_t *src, int32_t *slot,
                    int32_t *order, int32_t *n_active, void *ws, size_t ws_bytes, void *stream);
 
+/* a1  moe_build_maps for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same maps, bit for bit, with no workspace
+ * argument.  Its scratch is a static device array of MOE_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends; nothing is allocated, on the device or the host,
+ * by this call (its first call on a device looks the array's address up).  n_invalid: NULL, or
+ * a device int32 [1] that receives the number of ids outside [0, E) (else that count lands in
+ * the scratch).  T*K above MOE_NOALLOC_MAX_ROUTES or E above MOE_MAX_E: MOE_EUNSUPPORTED.  Every
+ * call on one GPU shares that GPU's array (each call rewrites all of it that it reads), so calls
+ * that overlap on one GPU, on any streams, race: serialise them. */
+#define MOE_NOALLOC_MAX_ROUTES (1 << 19)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)4196608)   /* 256 + 512 chunks x 2049 bins x 4 B */
+int moe_build_maps_noalloc(const int32_t *topk_idx, int T, int K, int E, int ring_start,
+                           int32_t *counts, int32_t *offsets, int32_t *src, int32_t *slot,
+                           int32_t *order, int32_t *n_active, int32_t *n_invalid, void *stream);
+
 /* a2  q8_1 quantisation of the layer input ([QS] opening section).
  * x fp32 [T x H] row-major; q8 [T*K x moe_q8_1_row_bytes(H)].
  * mode without MOE_QUANT_PER_ROW (scatter): each token row is read once and written to rows

@@ -45,6 +45,7 @@ SIGNATURES = {
     "moe_workspace_size": (SZ, [I, I, I, I, I, I, I]),
     "moe_route_topk": (I, [P, I, I, I, P, P, P]),
     "moe_build_maps": (I, [P, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
+    "moe_build_maps_noalloc": (I, [P, I, I, I, I, P, P, P, P, P, P, P, P]),
     "moe_quantize_scatter_q8_1": (I, [P, I, I, I, P, P, I, P, P]),
     "moe_gather_group": (I, [P, I, SZ, P, I, SZ, P]),
     "moe_gather_group_mmq": (I, [P, I, I, I, I, P, I, SZ, P]),
@@ -156,6 +157,18 @@ def build_maps(topk_idx, E, ring_start, counts, offsets, src, slot, order, n_act
     _check("moe_build_maps", lib().moe_build_maps(
         _ptr(topk_idx), T, K, E, ring_start, _ptr(counts), _ptr(offsets), _ptr(src), _ptr(slot),
         _ptr(order), _ptr(n_active), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def raw_build_maps_noalloc(topk_idx, E, ring_start, counts, offsets, src, slot, order,
+                           n_active, n_invalid=None, stream=None):
+    T, K = topk_idx.shape
+    return lib().moe_build_maps_noalloc(
+        _ptr(topk_idx), T, K, E, ring_start, _ptr(counts), _ptr(offsets), _ptr(src), _ptr(slot),
+        _ptr(order), _ptr(n_active), _ptr(n_invalid), _stream(stream))
+
+
+def build_maps_noalloc(*args, **kw):
+    _check("moe_build_maps_noalloc", raw_build_maps_noalloc(*args, **kw))
 
 
 def quantize_scatter_q8_1(x, K, slot, src, mode, q8, stream=None):

@@ -112,6 +112,24 @@ int moe_build_maps(const int32_t* topk_idx, int T, int K, int E, int ring_start,
   return status_of(launch_build_maps(topk_idx, T, K, E, ring_start, o, as_stream(stream)));
 }
 
+int moe_build_maps_noalloc(const int32_t* topk_idx, int T, int K, int E, int ring_start,
+                           int32_t* counts, int32_t* offsets, int32_t* src, int32_t* slot,
+                           int32_t* order, int32_t* n_active, int32_t* n_invalid, void* stream) {
+  static_assert(MOE_NOALLOC_MAX_ROUTES == kNoAllocMaxRoutes && MOE_MAX_E == kNoAllocMaxE,
+                "the header's limits are the scratch array's");
+  static_assert(MOE_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "the stated scratch size");
+  if (!topk_idx || !counts || !offsets || !src || !slot || !order || !n_active)
+    return MOE_EINVAL;
+  if (T < 1 || K < 1 || E < 1 || K > E || ring_start < 0 || ring_start >= E) return MOE_EINVAL;
+  if ((long long)T * K > MOE_NOALLOC_MAX_ROUTES || E > MOE_MAX_E) return MOE_EUNSUPPORTED;
+  uint8_t* sc = nullptr;
+  if (noalloc_scratch(&sc) != hipSuccess) return MOE_EHIP;
+  MapsOut o{counts, offsets, src, slot, order, n_active,
+            reinterpret_cast<int32_t*>(sc + kMapsHistAt), nullptr, nullptr, kMmqRows,
+            n_invalid != nullptr ? n_invalid : reinterpret_cast<int32_t*>(sc), nullptr};
+  return status_of(launch_build_maps(topk_idx, T, K, E, ring_start, o, as_stream(stream)));
+}
+
 int moe_quantize_scatter_q8_1(const float* x, int T, int H, int K, const int32_t* slot,
                               const int32_t* src, int mode, void* q8, void* stream) {
   if (!x || !q8 || T < 1 || K < 1 || mode < 0 || mode > (MOE_QUANT_PER_ROW | MOE_QUANT_D4))

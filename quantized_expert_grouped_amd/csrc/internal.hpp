@@ -41,6 +41,15 @@ struct MapsOut {
 // Scratch of moe_build_maps: the status words in the first 256 bytes, then hist.
 constexpr size_t kMapsHistAt = 256;
 inline size_t maps_hist_bytes(int R, int E) { return (size_t)map_chunks(R) * (E + 1) * 4; }
+
+// moe_build_maps_noalloc: its scratch is a static device array of fixed size (maps.hip).
+constexpr int kNoAllocMaxRoutes = 1 << 19;   // T*K
+constexpr int kNoAllocMaxE = 2048;
+constexpr size_t kNoAllocScratchBytes =
+    kMapsHistAt + (((size_t)((kNoAllocMaxRoutes + kMapChunk - 1) / kMapChunk) * (kNoAllocMaxE + 1) *
+                    4 + 255) / 256) * 256;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(uint8_t** out);
 hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_start,
                              const MapsOut& o, hipStream_t s);
 inline int max_mtiles(int R, int E, int tile_rows) { return R / tile_rows + (E < R ? E : R); }

@@ -15,8 +15,16 @@
 // with src = -1 for those rows and slot = -1 for the entries, so every later step can skip
 // them (the quantiser writes no row for them, the combine adds nothing for them), and the scan
 // stores their number in the status word at the front of the scratch buffer.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
+
+// The scratch of moe_build_maps_noalloc: the status words and the per-chunk histograms for up to
+// kNoAllocMaxRoutes routes of up to MOE_MAX_E experts, held by each GPU the library runs on until
+// the process ends.  In host code this name is only a stand-in for the symbol: the device
+// address is what hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[moe::kNoAllocScratchBytes];
 
 namespace moe {
 
@@ -234,6 +242,26 @@ hipError_t launch_build_maps(const int32_t* idx, int T, int K, int E, int ring_s
   maps_scatter_kernel<<<blocks, 256, lds, s>>>(idx, R, E, nbits, nchunks, o.hist, o.offsets,
                                                o.src, o.slot);
   return hipGetLastError();
+}
+
+// This device's address of `scratch`, looked up once per device (with that device current) and
+// kept; every later call on the device uses the kept address.
+hipError_t noalloc_scratch(uint8_t** out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(ptr[dev]);
+  return hipSuccess;
 }
 
 }  // namespace moe
