@@ -22,6 +22,8 @@ Other lines (not the headline; each prints its own JSON line):
     --cold-mib N        cold cache: N MiB of scratch written between steps (512 or more flushes
                         the 256 MB MALL and the L2s), each step timed by events around it.
     --copy-probe-mib N  one plain copy before the steps (the traffic counters' calibration).
+    --quant-ab          the q8_1 quantiser alone: per-row gather against scatter at 2,048 /
+                        8,192 / 32,768 tokens x 10 rows, warm and cold.
 """
 from __future__ import annotations
 
@@ -79,42 +81,50 @@ def algorithmic_work(c, n_active: int):
     }
 
 
-KERNEL_SOURCES = ("quantized_expert_grouped_amd/csrc/mmq.hip",
-                  "quantized_expert_grouped_amd/csrc/common.hpp",
-                  "quantized_expert_grouped_amd/csrc/internal.hpp")
-STAGE_KERNEL = {"gate_up": "mmq_gate_up", "down": "mmq_down"}
+CSRC = "quantized_expert_grouped_amd/csrc/"
+# the sources each stage's kernel is built from (a traffic figure is valid while they are)
+STAGE_SOURCES = {
+    "route": ("route.hip", "common.hpp"),
+    "maps": ("maps.hip", "common.hpp", "internal.hpp"),
+    "quantize": ("quantize.hip", "common.hpp"),
+    "gather": ("gather.hip", "common.hpp"),
+    "gate_up": ("mmq.hip", "common.hpp", "internal.hpp"),
+    "down": ("mmq.hip", "common.hpp", "internal.hpp"),
+    "combine": ("combine.hip", "common.hpp"),
+}
 
 
-def kernel_source_hash() -> str:
+def stage_source_hash(stage: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in STAGE_SOURCES[stage]:
+        with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+
+
 def measured_traffic(stage: str, workload: str):
     """HBM-side bytes per launch of a stage's kernel from the committed counter summary
-    (profiles/<kernel>_<workload>_traffic.txt), or None when there is none or the kernel
-    sources have changed since the counters were taken."""
-    kern = STAGE_KERNEL.get(stage)
-    if kern is None:
+    (profiles/traffic_<workload>.txt, lines ``traffic <stage> <bytes> <source hash>``), or None
+    when there is none or the stage's kernel sources have changed since the counters were
+    taken."""
+    path = traffic_path(workload)
+    if stage not in STAGE_SOURCES or not os.path.exists(path):
         return None
-    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
     with open(path) as fh:
         for line in fh:
-            if ":" in line and not line.startswith((" ", "#", "|")):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != kernel_source_hash():
-        return None
-    try:
-        return int(float(kv["hbm_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+            f = line.split()
+            if len(f) == 4 and f[0] == "traffic" and f[1] == stage:
+                if f[3] != stage_source_hash(stage):
+                    return None
+                try:
+                    return int(f[2])
+                except ValueError:
+                    return None
+    return None
 
 
 def copy_probe(mib: int, dev) -> None:
@@ -333,6 +343,85 @@ def graph_steps(args, c, layer, x, logits, out, dev):
     print(json.dumps(line))
 
 
+QUANT_AB_TOKENS = (2048, 8192, 32768)
+
+
+def quant_ab(args, dev):
+    """The q8_1 quantiser alone, the per-row gather form against the scatter form ("#1368
+    prefill: quantize each token's MoE input once and scatter it to its k rows", "Measured":
+    2,048 / 8,192 / 32,768 tokens x 10 rows, median of 20), H = 2048, 10 of 512 experts routed
+    by the GPU from N(0,1) logits (the t2k / t8k / t32k draws).  Warm: the launches back to back;
+    cold: --cold-mib MiB of scratch written before each launch.  Each launch is timed by HIP
+    events around it on the current stream.  Prints one JSON line."""
+    import torch
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(max(args.cold_mib, 1024) << 20, dtype=torch.uint8, device=dev)
+    results = []
+    for T, name in zip(QUANT_AB_TOKENS, ("t2k", "t8k", "t32k")):
+        c = synth.config_case(name, with_pool=False)
+        K, H, E = c.K, c.H, c.E
+        x = torch.from_numpy(c.x).to(dev)
+        logits = torch.from_numpy(c.logits).to(dev)
+        idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        abi.route_topk(logits, K, idx, w)
+        R = T * K
+        mk = lambda n, dt=torch.int32: torch.empty(n, dtype=dt, device=dev)
+        m = dict(counts=mk(E), offsets=mk(E + 1), src=mk(R), slot=mk(R), order=mk(E),
+                 n_active=mk(1))
+        ws = mk(abi.build_maps_workspace_size(T, K, E), torch.uint8)
+        abi.build_maps(idx, E, 0, m["counts"], m["offsets"], m["src"], m["slot"], m["order"],
+                       m["n_active"], ws)
+        q8 = torch.empty((R, abi.q8_1_row_bytes(H)), dtype=torch.uint8, device=dev)
+        row = {"T": T, "rows": R}
+        for cache in ("warm", "cold"):
+            for mode_name, mode in (("gather", abi.QUANT_PER_ROW), ("scatter", 0)):
+                for _ in range(3):
+                    abi.quantize_scatter_q8_1(x, K, m["slot"], m["src"], mode, q8)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.steps)]
+                for i in range(args.steps):
+                    if cache == "cold":
+                        flush.fill_(i & 0xFF)
+                    ev[i][0].record(stream)
+                    abi.quantize_scatter_q8_1(x, K, m["slot"], m["src"], mode, q8)
+                    ev[i][1].record(stream)
+                torch.cuda.synchronize()
+                ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+                reads = 4 * T * H * (K if mode == abi.QUANT_PER_ROW else 1) + 4 * R
+                row[f"{cache}_{mode_name}_ms"] = round(ms, 4)
+                row[f"{cache}_{mode_name}_gbs"] = round((reads + R * abi.q8_1_row_bytes(H)) /
+                                                        (ms * 1e-3) / 1e9, 1)
+            row[f"{cache}_gather_over_scatter"] = round(row[f"{cache}_gather_ms"] /
+                                                        row[f"{cache}_scatter_ms"], 3)
+        results.append(row)
+        del x, logits, q8, ws
+        torch.cuda.empty_cache()
+    line = {
+        "metric": "q8_1 quantiser time, per-row gather over scatter (T x 10 rows, H = 2048), "
+                  "cold cache, largest T",
+        "value": results[-1]["cold_gather_over_scatter"],
+        "unit": "x",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 3,
+        "ms_per_step": results[-1]["cold_scatter_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32->int8",
+        "data": "synthetic",
+        "config": {"workload": "quantize-scatter vs per-row gather: T = 2048, 8192, 32768; "
+                               "H = 2048, K = 10 of E = 512 (t2k / t8k / t32k draws)",
+                   "cold_mib": max(args.cold_mib, 1024),
+                   "clock": "HIP events around each launch, median of --steps launches"},
+        "results": results,
+        "roofline": None,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,6 +454,9 @@ def main():
     ap.add_argument("--cold-mib", type=int, default=0,
                     help="write this many MiB of scratch between steps (cache flush) and time "
                          "each step with events around it (another line, not the headline)")
+    ap.add_argument("--quant-ab", action="store_true",
+                    help="the q8_1 quantiser alone, per-row gather against scatter, at 2,048 / "
+                         "8,192 / 32,768 tokens x 10 rows, warm and cold (another line)")
     ap.add_argument("--act-d4", action="store_true",
                     help="a Q8_0 workload with its activations in the D4 q8_1 layout (fp32 "
                          "scales) instead of DS4")
@@ -381,6 +473,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.quant_ab:
+        quant_ab(args, dev)
+        return
     c = synth.config_case(args.workload)
     if args.act_d4:
         if c.wtype != synth.Q8_0:
@@ -462,26 +557,43 @@ def main():
                     entry["tops"] = round(amt / (t_ms * 1e-3) / 1e12, 2)
                     entry["frac_i8_peak"] = round(entry["tops"] / PEAK_I8_TOPS, 4)
                     kb, bb = work[name + "_bytes"]
+                    roof = min(PEAK_I8_TOPS, amt / bb * PEAK_HBM_GBS / 1e3)
+                    entry["frac_ai_roof"] = round(entry["tops"] / roof, 4)
                     entry["gbs"] = round(bb / (t_ms * 1e-3) / 1e9, 1)
                 else:
                     entry["gbs"] = round(amt / (t_ms * 1e-3) / 1e9, 1)
                     entry["frac_hbm_peak"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
             stages[name] = entry
+        for name, entry in stages.items():
+            tb = measured_traffic(name, c.name)
+            if tb is not None and name in work:
+                alg = work[name + "_bytes"][1] if work[name][0] == "ops" else work[name][1]
+                entry["traffic_bytes"] = tb
+                entry["traffic_ratio"] = round(tb / alg, 3)
         dom = max(avg, key=avg.get)
         kind, amt = work.get(dom, ("bytes", 4 * c.R))
         t_s = avg[dom] * 1e-3
+        clock = ("HIP events on the layer's stream around each launch (they add the event "
+                 "records' gap; the kernel trace in profiles/ times the kernel alone)")
         if kind == "ops":
             achieved = amt / t_s / 1e12
+            alg_bytes = work[dom + "_bytes"][1]
+            roof = min(PEAK_I8_TOPS, amt / alg_bytes * PEAK_HBM_GBS / 1e3)
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                        "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                        "peak": PEAK_I8_TOPS, "unit": "TOP/s",
                         "frac": round(achieved / PEAK_I8_TOPS, 4),
-                        "traffic": measured_traffic(dom, c.name)}
+                        "traffic": measured_traffic(dom, c.name),
+                        "algorithmic_ops": amt, "algorithmic_bytes": alg_bytes,
+                        "ai_roof": round(roof, 1), "frac_ai_roof": round(achieved / roof, 4),
+                        "launch_ms": round(avg[dom], 4), "clock": clock}
         else:
             achieved = amt / t_s / 1e9
             roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(achieved / PEAK_HBM_GBS, 4),
-                        "traffic": measured_traffic(dom, c.name)}
+                        "traffic": measured_traffic(dom, c.name),
+                        "algorithmic_bytes": amt, "launch_ms": round(avg[dom], 4),
+                        "clock": clock}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -132,7 +132,9 @@ def make_pool(rng: np.random.Generator, E: int, H: int, F: int, wtype: int, perm
 
 def make_case(name: str = "custom", *, T: int, H: int, F: int, E: int, K: int, wtype: int,
               seed: int, zero_tokens=(), zipf: float | None = None, ring_start=None,
-              group_size: int = 16) -> Case:
+              group_size: int = 16, with_pool: bool = True) -> Case:
+    """``with_pool=False`` draws x and the logits only (the pool is left empty), for measurements
+    of the steps that do not read the experts."""
     ss = np.random.SeedSequence(seed)
     s_x, s_logit, s_w, s_perm, s_ring, s_zipf, s_zero = ss.spawn(7)
     rx = np.random.default_rng(s_x)
@@ -148,8 +150,14 @@ def make_case(name: str = "custom", *, T: int, H: int, F: int, E: int, K: int, w
         bias = np.empty(E, np.float64)
         bias[zperm] = -zipf * np.log(np.arange(1, E + 1, dtype=np.float64))
         logits = (logits + bias.astype(np.float32)[None, :]).astype(np.float32)
-    pool, expert_off, eb, stride = make_pool(np.random.default_rng(s_w), E, H, F, wtype,
-                                             np.random.default_rng(s_perm))
+    if with_pool:
+        pool, expert_off, eb, stride = make_pool(np.random.default_rng(s_w), E, H, F, wtype,
+                                                 np.random.default_rng(s_perm))
+    else:
+        eb = expert_bytes(H, F, wtype)
+        stride = round_up(eb, 256)
+        pool = np.zeros(0, np.uint8)
+        expert_off = np.random.default_rng(s_perm).permutation(E).astype(np.int64) * stride
     if ring_start is None:
         ring_start = int(np.random.default_rng(s_ring).integers(1, E)) if E > 1 else 0
     return Case(name=name, T=T, H=H, F=F, E=E, K=K, wtype=wtype, x=x, logits=logits, pool=pool,
@@ -157,14 +165,14 @@ def make_case(name: str = "custom", *, T: int, H: int, F: int, E: int, K: int, w
                 ring_start=int(ring_start), group_size=group_size, zero_tokens=zero_tokens)
 
 
-def config_case(name: str, T: int | None = None) -> Case:
+def config_case(name: str, T: int | None = None, with_pool: bool = True) -> Case:
     """One of the named workloads (seed 1000 + its number).  ``T`` may shorten the chunk
     (its first T tokens keep the same rows of x and logits)."""
     c = dict(CONFIGS[name])
     no = c.pop("no")
     zero = c.pop("zero_tokens", ())
     zipf = c.pop("zipf", None)
-    case = make_case(name, seed=1000 + no, zero_tokens=zero, zipf=zipf, **c)
+    case = make_case(name, seed=1000 + no, zero_tokens=zero, zipf=zipf, with_pool=with_pool, **c)
     if T is not None and T < case.T:
         case.x = case.x[:T].copy()
         case.logits = case.logits[:T].copy()

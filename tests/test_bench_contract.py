@@ -40,16 +40,27 @@ def test_algorithmic_work_t8k():
     assert w["route"] == ("bytes", 4 * 8192 * 512 + 8 * R)
 
 
-def test_traffic_figure_follows_the_source_hash(monkeypatch):
-    path = os.path.join(ROOT, "profiles", "mmq_gate_up_t8k_traffic.txt")
-    if not os.path.exists(path):
-        pytest.skip("no committed traffic summary")
-    text = open(path).read()
-    want = [l for l in text.splitlines() if l.startswith("hbm_bytes_per_launch:")]
-    assert want
-    if f"source_sha256: {bench.kernel_source_hash()}" in text:
-        assert bench.measured_traffic("gate_up", "t8k") == int(want[0].split(":")[1])
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+def test_traffic_figure_follows_the_source_hash(tmp_path, monkeypatch):
+    """A stage's traffic is read from profiles/traffic_<workload>.txt only while the hash of that
+    stage's kernel sources matches the one recorded beside it."""
+    p = tmp_path / "traffic_t8k.txt"
+    p.write_text("# header\n"
+                 f"traffic gate_up 929143756 {bench.stage_source_hash('gate_up')}\n"
+                 f"traffic combine 738000000 {'0' * 16}\n")
+    monkeypatch.setattr(bench, "traffic_path", lambda w: str(p) if w == "t8k" else "/nonexistent")
+    assert bench.measured_traffic("gate_up", "t8k") == 929143756
+    assert bench.measured_traffic("combine", "t8k") is None        # stale hash
+    assert bench.measured_traffic("quantize", "t8k") is None       # no line
+    assert bench.measured_traffic("gate_up", "t2k") is None        # no file
+    monkeypatch.setattr(bench, "stage_source_hash", lambda st: "1" * 16)
     assert bench.measured_traffic("gate_up", "t8k") is None
-    assert bench.measured_traffic("combine", "t8k") is None
-    assert bench.measured_traffic("gate_up", "no_such_workload") is None
+
+
+def test_committed_traffic_summaries_parse():
+    """Every committed summary's traffic lines name a known stage, a byte count and a hash."""
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.txt")):
+        lines = [l.split() for l in open(path) if l.startswith("traffic ")]
+        assert lines, path
+        for f in lines:
+            assert len(f) == 4 and f[1] in bench.STAGE_SOURCES and int(f[2]) > 0 and len(f[3]) == 16

@@ -20,6 +20,7 @@ MODES = [
     ("graph", ["--graph"]),
     ("cold", ["--cold-mib", "64"]),
     ("d4", ["--act-d4"]),
+    ("quant_ab", ["--quant-ab"]),
 ]
 
 
@@ -39,11 +40,15 @@ def test_bench_mode_prints_one_contract_line(mode):
         assert key in b, key
     assert b["n_gpus"] == 1 and b["steps"] == 3 and b["warmup"] == 1
     assert b["value"] > 0 and b["ms_per_step"] > 0
+    if name == "quant_ab":        # its own sizes: the quantiser page's 2K / 8K / 32K tokens
+        assert [r["T"] for r in b["results"]] == [2048, 8192, 32768]
+        assert all(r["cold_scatter_ms"] > 0 and r["warm_gather_ms"] > 0 for r in b["results"])
+        return
     assert b["config"]["workload"].startswith("tiny")
     if name == "default":  # (the tiny case's fractions round to zero)
         rf = b["roofline"]
         for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
             assert key in rf, key
-        assert rf["unit"] in ("TFLOP/s", "GB/s") and rf["peak"] > 0 and rf["frac"] >= 0
+        assert rf["unit"] in ("TOP/s", "GB/s") and rf["peak"] > 0 and rf["frac"] >= 0
     if name == "cold":
         assert "cold" in b["metric"] and "cache" in b["config"]
