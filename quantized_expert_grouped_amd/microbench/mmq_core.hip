@@ -18,6 +18,8 @@
 //                    of the convert (exact for |I| < 2^22)
 //   pipelined        block b+1's MFMAs interleaved with block b's convert + fma (two register
 //                    sets), one MFMA then 16 VALU ops
+//   i8 into AGPRs    the int8 MFMAs write accumulation registers (inline asm), each element is
+//                    read back before its convert
 // each at 2, 3 and 4 wavefronts per SIMD (set by the LDS a workgroup reserves).
 #include <hip/hip_runtime.h>
 #include <stdio.h>
@@ -111,9 +113,10 @@ double rate(int ncu, const int* din, float* dout, double macs, int per_iter, dou
 }
 
 // ---- part 2 ------------------------------------------------------------------------------------
-enum { M_FULL, M_NOCVT, M_NOF16, M_NOI8, M_MFMA, M_VALU, M_BIAS, M_PIPE, M_COUNT };
+enum { M_FULL, M_NOCVT, M_NOF16, M_NOI8, M_MFMA, M_VALU, M_BIAS, M_PIPE, M_AGPR, M_COUNT };
 static const char* kMixName[M_COUNT] = {"full", "no convert", "no f16 MFMA", "no i8 MFMA",
-                                        "MFMAs only", "VALU only", "bias + add", "pipelined"};
+                                        "MFMAs only", "VALU only", "bias + add", "pipelined",
+                                        "i8 into AGPRs"};
 
 template <int M, int W>
 __global__ __launch_bounds__(256, W) void mix_kernel(const int* __restrict__ in,
@@ -192,6 +195,9 @@ __global__ __launch_bounds__(256, W) void mix_kernel(const int* __restrict__ in,
       } else if (M == M_BIAS) {
         I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, ibias, 0, 0, 0);
         I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, ibias, 0, 0, 0);
+      } else if (M == M_AGPR) {  // results in accumulation registers, read back per element
+        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0" : "=a"(I0) : "v"(a), "v"(b0));
+        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0" : "=a"(I1) : "v"(a), "v"(b1));
       } else {
         I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
         I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
@@ -304,6 +310,7 @@ int main() {
   mix_row<M_VALU>(ncu, din, dout);
   mix_row<M_BIAS>(ncu, din, dout);
   mix_row<M_PIPE>(ncu, din, dout);
+  mix_row<M_AGPR>(ncu, din, dout);
   const hipError_t e = hipDeviceSynchronize();
   printf("\nstatus %s\n", hipGetErrorString(e));
   return e == hipSuccess ? 0 : 1;
