@@ -216,6 +216,10 @@ def streamed_walk(args, c, layer, x, logits, out, dev):
     resident = [base + int(c.expert_off[e]) if e in keep else 0 for e in range(c.E)]
     flags = abi.WALK_GATHER_ONE if args.gather_one else 0
     G = args.walk_group_size
+    share = None
+    if args.cpu_share is not None:
+        share = -1.0 if args.cpu_share == "auto" else float(args.cpu_share)
+        walk.cpu_share(share, args.cpu_share_max_tokens, args.cpu_threads, c.T, c.H, c.T * c.K)
 
     def step():
         idx, w = layer.route(logits)
@@ -232,7 +236,8 @@ def streamed_walk(args, c, layer, x, logits, out, dev):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     st1 = walk.stats()
-    d = {k: (st1[k] - st0[k]) / args.steps for k in st1}
+    last = ("share_ppm", "gpu_ns_per_expert", "host_ns_per_expert")   # the last call's values
+    d = {k: (st1[k] if k in last else (st1[k] - st0[k]) / args.steps) for k in st1}
     pcie = h2d_probe(1024, dev)
     walk.close()
     ms_per_step = elapsed * 1e3 / args.steps
@@ -250,9 +255,16 @@ def streamed_walk(args, c, layer, x, logits, out, dev):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}", "walk": "streamed",
+        "config": {"workload": f"{c.name}: {WORKLOAD_DOC[c.name]}"
+                               + (f", first {c.T} tokens" if args.tokens else ""),
+                   "T": c.T, "walk": "streamed",
                    "ring_slots": args.ring_slots, "resident_experts": n_res,
-                   "group_size": G, "gather_one": bool(args.gather_one)},
+                   "group_size": G, "gather_one": bool(args.gather_one),
+                   "cpu_share": args.cpu_share,
+                   **({"cpu_share_max_tokens": args.cpu_share_max_tokens,
+                       "cpu_share_isa": abi.cpu_share_isa(),
+                       "cpu_share_threads": args.cpu_threads or os.cpu_count()}
+                      if args.cpu_share is not None else {})},
         "roofline": {"kernel": "host->device expert copies (copy stream)", "bound": "pcie",
                      "achieved": round(h2d, 2), "peak": PEAK_PCIE_GBS, "unit": "GB/s",
                      "frac": round(h2d / PEAK_PCIE_GBS, 4), "traffic": None,
@@ -448,6 +460,15 @@ def main():
     ap.add_argument("--walk-group-size", type=int, default=16)
     ap.add_argument("--gather-one", action="store_true",
                     help="streamed walk: one gather launch, wait and event per expert")
+    ap.add_argument("--cpu-share", default=None,
+                    help="streamed walk: hand the least-routed streamed experts to host threads, "
+                         "a fixed share in (0, 1] or 'auto' (g / (c + g) from measured rates)")
+    ap.add_argument("--cpu-share-max-tokens", type=int, default=0,
+                    help="streamed walk with --cpu-share: only experts routed by at most this "
+                         "many tokens (0: any)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="the workload's first N tokens only (small chunks: the CPU share's "
+                         "regime); not the headline")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step (routing + the layer) in a HIP graph and time its "
                          "replays (another line, not the headline)")
@@ -476,7 +497,7 @@ def main():
     if args.quant_ab:
         quant_ab(args, dev)
         return
-    c = synth.config_case(args.workload)
+    c = synth.config_case(args.workload, T=args.tokens or None)
     if args.act_d4:
         if c.wtype != synth.Q8_0:
             print("bench.py: --act-d4 applies to the Q8_0 workloads", file=sys.stderr)

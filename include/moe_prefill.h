@@ -317,14 +317,50 @@ int moe_prefill_layer_streamed(moe_walk *walk, const float *x, int T, int H, int
  *   5 batches launched for a skipped entry,
  *   6 batches launched for a ring slot held by the open batch, 7 MMQ launches, 8 routing syncs,
  *   9 host->device transfers (consecutive copies of one batch whose experts lie slot_stride apart
- *     in the arena and land in consecutive slots go out as one transfer).
+ *     in the arena and land in consecutive slots go out as one transfer),
+ *   the CPU share (moe_walk_cpu_share): 10 experts the host computed, 11 their routed rows,
+ *   12 host compute time in microseconds, and of the last call 13 the share used (x 10^6),
+ *   14 the GPU's measured time per streamed expert (ns), 15 the host's (ns); 0 = not measured.
  * Writes min(n, MOE_WALK_NSTATS) entries. */
-#define MOE_WALK_NSTATS 10
+#define MOE_WALK_NSTATS 16
 int moe_walk_stats(const moe_walk *walk, int64_t *stats, int n);
+
+/* The CPU share of a walk ("#1282 prefill: STRATA_PREFILL_CPU_SHARE=auto hands a small chunk's
+ * least-routed experts to the idle CPU pool", "What it does"), opt-in; off unless this is called.
+ * From the next moe_prefill_layer_streamed on, after the routing sync, the streamed (non-resident)
+ * routed experts routed by at most max_tokens tokens (0: any count), fewest first, up to
+ * share x (the call's streamed routed experts), are computed on the host: a pool of `threads` host
+ * threads (0: all the host has) reads them from the arena and the call's x and src (copied to the
+ * host before the routing sync) and computes their unweighted rows (q8_1 of x, gate/up, SwiGLU,
+ * q8_1 of h, down) while the GPU streams and computes the rest; the GPU neither copies, gathers
+ * nor multiplies them.  The rows are staged contiguously, copied to the device once and put into
+ * their Dm rows, and the combine weights them as any other row.  The host's integer dots are the
+ * GPU's; its fp32 sums run in another order, so the output is within fp32 rounding of the GPU's,
+ * not bit-identical.  The call blocks until the host's part is done (besides the routing sync).
+ *   share: in (0, 1] a fixed share; < 0 automatic: 0.25 first, then g / (c + g) from the
+ *          previous call's measured GPU time per streamed expert (g, events around its expert
+ *          work) and host time per expert (c); 0 turns the share off and frees its buffers.
+ *   max_T, H: the largest T and the H of the calls (a call outside them returns MOE_EINVAL);
+ *   max_rows: at most this many rows per call go to the host (its staging capacity).
+ * Allocates pinned host buffers (max_T x H and max_rows x H fp32), device buffers (max_rows x H
+ * fp32) and starts the threads; MOE_EHIP if they cannot be made (the previous setting stays).
+ * Not a fallback: the HIP path never hands work to the host unless the caller asks for it here. */
+int moe_walk_cpu_share(moe_walk *walk, double share, int max_tokens, int threads, int max_T,
+                       int H, int max_rows);
+
+/* The host's computation for one expert, as the CPU share runs it ([CS] "What it does"): the
+ * unweighted rows of n_rows inputs through a raw expert.  All pointers [host]: expert
+ * moe_expert_bytes(H, F, wtype) bytes, x fp32 [n_rows x H], out fp32 [n_rows x H].  Runs on the
+ * calling thread.  H, F multiples of 128. */
+int moe_cpu_expert_rows(int wtype, int H, int F, const void *expert, const float *x, int n_rows,
+                        float *out);
+/* The host instruction set the CPU share's dot products use: "avx512-vnni", "avx2" or "scalar". */
+const char *moe_cpu_share_isa(void);
 
 /* The walk's schedule alone, computed on the host as moe_prefill_layer_streamed computes it
  * (nothing is enqueued; no device is needed).  Inputs [host]: counts int32 [E], order int32 [E]
- * and n_active as moe_build_maps returns them; streamed uint8 [E] (1 = copied from the arena);
+ * and n_active as moe_build_maps returns them; streamed uint8 [E] (1 = copied from the arena,
+ * 2 = computed by the host: never copied nor gathered, its position kept);
  * group_size, n_slots, flags as above.  State in/out [host]: used_of int32 [n_slots] (the event
  * of each slot's last reader batch, -1 = never read), cursor (next ring slot, 0..n_slots-1),
  * next_event (the event the next batch records, 0..MOE_WALK_EVENTS-1).  ops [host] int32 [max_ops x 6],
@@ -333,7 +369,8 @@ int moe_walk_stats(const moe_walk *walk, int64_t *stats, int n);
  *   {2, first_pos, n, waits (0/1), event, why}               gather batch of positions
  *                                                            first_pos .. first_pos+n-1;
  *                                                            why: 0 group complete, 1 skipped
- *                                                            entry, 2 slot held, 3 one expert
+ *                                                            entry, 2 slot held, 3 one expert,
+ *                                                            4 a host-computed expert follows
  *   {3, group, first_pos, n, 0, 0}                           MMQ of the group's positions
  * Returns the number of records, MOE_EINVAL (inconsistent inputs) or MOE_EWORKSPACE (max_ops too
  * small; the state is then unspecified). */

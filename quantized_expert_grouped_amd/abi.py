@@ -25,9 +25,10 @@ STAGES = ("maps", "quantize", "gather", "gate_up", "down", "combine")
 
 WALK_EVENTS = 64
 WALK_GATHER_ONE, WALK_NO_SKIP_FLUSH = 1, 2
-WALK_NSTATS = 10
+WALK_NSTATS = 16
 WALK_STATS = ("copies", "bytes", "batches", "waits", "copy_waits", "skip_flushes", "slot_flushes",
-              "mmq_launches", "routing_syncs", "transfers")
+              "mmq_launches", "routing_syncs", "transfers", "host_experts", "host_rows",
+              "host_us", "share_ppm", "gpu_ns_per_expert", "host_ns_per_expert")
 OP_COPY, OP_GATHER, OP_MMQ = 1, 2, 3
 
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EWORKSPACE",
@@ -59,6 +60,9 @@ SIGNATURES = {
     "moe_prefill_layer_streamed": (I, [P, P, I, I, I, I, I, P, P, I, P, SZ, P, P, I, I, I, P, SZ,
                                        P, P]),
     "moe_walk_stats": (I, [P, P, I]),
+    "moe_walk_cpu_share": (I, [P, ctypes.c_double, I, I, I, I, I]),
+    "moe_cpu_expert_rows": (I, [I, I, I, P, P, I, P]),
+    "moe_cpu_share_isa": (ctypes.c_char_p, []),
     "moe_walk_plan": (I, [P, P, I, I, I, P, I, I, I, P, P, P, P, I]),
     "moe_profile_begin": (I, [I]),
     "moe_profile_end": (I, [P, I]),
@@ -289,6 +293,13 @@ class Walk:
         except Exception:
             pass
 
+    def cpu_share(self, share: float, max_tokens: int, threads: int, max_T: int, H: int,
+                  max_rows: int) -> None:
+        """The host's share of the walk (share < 0: automatic; 0: off)."""
+        _check("moe_walk_cpu_share", lib().moe_walk_cpu_share(self.handle, float(share),
+                                                              max_tokens, threads, max_T, H,
+                                                              max_rows))
+
     def stats(self) -> dict:
         a = np.zeros(WALK_NSTATS, np.int64)
         _check("moe_walk_stats", lib().moe_walk_stats(self.handle,
@@ -317,6 +328,22 @@ def raw_prefill_layer_streamed(walk, x, topk_idx, topk_w, wtype, host_arena, hos
 
 def prefill_layer_streamed(*args, **kw):
     _check("moe_prefill_layer_streamed", raw_prefill_layer_streamed(*args, **kw))
+
+
+def cpu_expert_rows(wtype, H, F, expert, x):
+    """The host's computation of one expert's unweighted rows (numpy in, numpy out)."""
+    expert = np.ascontiguousarray(expert, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty((x.shape[0], H), np.float32)
+    vp = ctypes.c_void_p
+    _check("moe_cpu_expert_rows", lib().moe_cpu_expert_rows(
+        wtype, H, F, expert.ctypes.data_as(vp), x.ctypes.data_as(vp), x.shape[0],
+        out.ctypes.data_as(vp)))
+    return out
+
+
+def cpu_share_isa() -> str:
+    return lib().moe_cpu_share_isa().decode()
 
 
 def walk_plan(counts, order, n_active, ring_start, streamed, group_size, n_slots, flags=0,

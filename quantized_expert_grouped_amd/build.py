@@ -20,7 +20,11 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_prefill.so")
 
 SOURCES = ["api.cpp", "walk.cpp", "route.hip", "maps.hip", "quantize.hip", "gather.hip",
-           "mmq.hip", "combine.hip"]
+           "mmq.hip", "combine.hip", "cpu_share.cpp"]
+# plain host code (no HIP): built by the host compiler
+HOST_SOURCES = {"cpu_share.cpp"}
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-ffp-contract=off", "-fno-fast-math",
+              "-Wall", "-I", CSRC]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -49,6 +53,12 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if src in HOST_SOURCES:
+        r = subprocess.run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"g++ failed for {src}:\n{r.stdout}{r.stderr}")
+        return obj
     cmd = [hipcc(), *FLAGS]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
@@ -68,7 +78,8 @@ def build(verbose: bool = True) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs,
+                        "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

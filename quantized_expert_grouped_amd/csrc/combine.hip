@@ -74,7 +74,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// One workgroup per staged row: 16-byte copies of the row into its place in Dm.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float* __restrict__ rows,
+                                                          const int32_t* __restrict__ dst, int H,
+                                                          float* __restrict__ Dm) {
+  const int j = blockIdx.x;
+  const v4f* src = reinterpret_cast<const v4f*>(rows + (size_t)j * H);
+  v4f* d = reinterpret_cast<v4f*>(Dm + (size_t)dst[j] * H);
+  for (int c = threadIdx.x; c < H / 4; c += 256) d[c] = src[c];
+}
+
 }  // namespace
+
+hipError_t launch_scatter_rows(const float* rows, const int32_t* dst, int n, int H, float* Dm,
+                               hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  scatter_rows_kernel<<<n, 256, 0, s>>>(rows, dst, H, Dm);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* Dm, const int32_t* slot, const float* w, int T, int K,
                           int H, float* out, hipStream_t s) {

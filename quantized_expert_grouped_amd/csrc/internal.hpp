@@ -108,6 +108,8 @@ struct MmqProblem {
   int tile_count;
   int n_tiles_n;          // weight-row tiles per m-tile (set by the launcher)
   int32_t* misaligned;    // layer form, packed pool: count of m-tiles skipped (or nullptr)
+  const uint8_t* skip;    // layer form: skip[e] != 0 -> expert e's tiles are not computed
+                          // (the host computes them), or nullptr
   // group form: positions j < n_group hold experts[j], rows from offsets
   const int32_t* offsets;
   int experts[16];
@@ -125,5 +127,8 @@ inline long long mmq_layer_workgroups(int n_out_gu, int n_out_dn, int max_tiles)
 // ---- a7 combine -----------------------------------------------------------------------------
 hipError_t launch_combine(const float* Dm, const int32_t* slot, const float* w, int T, int K,
                           int H, float* out, hipStream_t s);
+// Dm[dst[j]] = rows[j] for j < n (fp32 rows of H values): the host's rows into their places.
+hipError_t launch_scatter_rows(const float* rows, const int32_t* dst, int n, int H, float* Dm,
+                               hipStream_t s);
 
 }  // namespace moe

@@ -456,6 +456,7 @@ __global__ __launch_bounds__(256, EPI == 2 ? 2 : kWgPerCu) void mmq_layer_kernel
   const int work = xcd * (live / kXcds) + min(xcd, live % kXcds) + id / kXcds;
   const int mt = work / ntl;
   const MTile t = p.tiles[mt];
+  if (p.skip != nullptr && p.skip[t.expert] != 0) return;  // the host computes this expert
   const uint8_t* W = p.mat_offset + (p.w_off != nullptr
                                          ? p.wbase + p.w_off[t.expert]
                                          : p.wbase + (size_t)t.ordinal * p.pos_stride);

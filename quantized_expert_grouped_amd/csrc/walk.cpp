@@ -13,9 +13,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
+#include <memory>
 #include <new>
+#include <thread>
 #include <vector>
 
+#include "cpu_share.hpp"
 #include "internal.hpp"
 #include "layout.hpp"
 #include "moe_prefill.h"
@@ -27,11 +31,14 @@ namespace {
 constexpr int kEvents = MOE_WALK_EVENTS;
 constexpr int kMaxE = MOE_MAX_E;
 enum { kOpCopy = 1, kOpGather = 2, kOpMmq = 3 };
-enum { kWhyGroup = 0, kWhySkip = 1, kWhySlot = 2, kWhyOne = 3 };
+enum { kWhyGroup = 0, kWhySkip = 1, kWhySlot = 2, kWhyOne = 3, kWhyHost = 4 };
+enum { kResident = 0, kStreamed = 1, kHost = 2 };  // an expert's state in the plan
 enum {
   kStCopies, kStBytes, kStBatches, kStWaits, kStCopyWaits, kStSkipFlush, kStSlotFlush, kStMmq,
-  kStSyncs, kStTransfers
+  kStSyncs, kStTransfers, kStHostExperts, kStHostRows, kStHostUs, kStSharePpm, kStGpuNs,
+  kStHostNs
 };
+static_assert(kStHostNs + 1 == MOE_WALK_NSTATS, "the header's counter list");
 
 struct Op {
   int32_t v[6];
@@ -41,7 +48,9 @@ struct Op {
 // next group position; a streamed one first takes the next ring slot (round robin) for its copy,
 // which waits on the event of that slot's last reader.  The open batch is launched when its group
 // is complete, at a skipped entry, when the next slot is one the open batch holds, or after every
-// expert (one-expert mode); a group's MMQ record follows its last batch.
+// expert (one-expert mode); a group's MMQ record follows its last batch.  An expert the host
+// computes (state kHost) keeps its position but is neither copied nor gathered: the open batch is
+// launched before it, since a batch is a run of consecutive positions.
 int plan(const int32_t* counts, const int32_t* order, int n_active, int E, int ring_start,
          const uint8_t* streamed, int G, int n_slots, int flags, int32_t* used_of,
          int32_t* cursor, int32_t* next_event, std::vector<Op>& ops) {
@@ -63,6 +72,8 @@ int plan(const int32_t* counts, const int32_t* order, int n_active, int E, int r
   if (j != n_active) return MOE_EINVAL;
   for (int s = 0; s < n_slots; ++s)
     if (used_of[s] < -1 || used_of[s] >= kEvents) return MOE_EINVAL;
+  for (int e = 0; e < E; ++e)
+    if (streamed[e] > kHost) return MOE_EINVAL;
 
   ops.clear();
   std::vector<char> held(n_slots, 0);  // the slot's copy belongs to the open batch
@@ -88,7 +99,16 @@ int plan(const int32_t* counts, const int32_t* order, int n_active, int E, int r
       if (!(flags & MOE_WALK_NO_SKIP_FLUSH)) flush(kWhySkip);
       continue;
     }
-    if (streamed[e]) {
+    if (streamed[e] == kHost) {
+      flush(kWhyHost);
+      ++pos;
+      if (pos % G == 0 || pos == n_active) {
+        ops.push_back({{kOpMmq, (pos - 1) / G, group_first, pos - group_first, 0, 0}});
+        group_first = pos;
+      }
+      continue;
+    }
+    if (streamed[e] == kStreamed) {
       const int s = *cursor;
       if (held[s]) flush(kWhySlot);
       ops.push_back({{kOpCopy, pos, e, s, used_of[s], 0}});
@@ -113,6 +133,48 @@ int plan(const int32_t* counts, const int32_t* order, int n_active, int E, int r
 
 }  // namespace
 
+namespace {
+
+// The CPU share of a walk: what the host computes, the buffers it stages through, and the two
+// per-expert rates the automatic share is set from.
+struct HostShare {
+  double share = 0;           // fixed share, or < 0: automatic
+  double cur = 0.25;          // the share the next call hands the host
+  int max_tokens = 0, T_max = 0, H = 0, rows_max = 0;
+  std::unique_ptr<CpuPool> pool;
+  std::vector<CpuScratch> scratch;
+  float* h_x = nullptr;       // pinned [T_max x H]: the layer input
+  int32_t* h_src = nullptr;   // pinned [T_max * MOE_MAX_K]: src
+  float* h_rows = nullptr;    // pinned [rows_max x H]: the host's rows
+  int32_t* h_dst = nullptr;   // pinned [rows_max]: each staged row's row in Dm
+  uint8_t* h_skip = nullptr;  // pinned [MOE_MAX_E]: 1 = the host computes the expert
+  float* d_rows = nullptr;    // device [rows_max x H]
+  int32_t* d_dst = nullptr;   // device [rows_max]
+  uint8_t* d_skip = nullptr;  // device [MOE_MAX_E]
+  hipEvent_t t0 = nullptr, t1 = nullptr;  // around the GPU's expert work (timing)
+  bool timed = false;         // t0/t1 were recorded by the previous call
+  int timed_experts = 0;      // streamed experts the GPU computed in that call
+  double gpu_ns = 0, host_ns = 0;  // measured time per expert, 0 = not yet
+};
+
+void free_host_share(HostShare* h) {
+  if (!h) return;
+  h->pool.reset();
+  if (h->t0) (void)hipEventDestroy(h->t0);
+  if (h->t1) (void)hipEventDestroy(h->t1);
+  for (void* p : {(void*)h->h_x, (void*)h->h_src, (void*)h->h_rows, (void*)h->h_dst,
+                  (void*)h->h_skip})
+    if (p) (void)hipHostFree(p);
+  for (void* p : {(void*)h->d_rows, (void*)h->d_dst, (void*)h->d_skip})
+    if (p) (void)hipFree(p);
+  h->h_x = h->h_rows = h->d_rows = nullptr;
+  h->h_src = h->h_dst = h->d_dst = nullptr;
+  h->h_skip = h->d_skip = nullptr;
+  h->t0 = h->t1 = nullptr;
+}
+
+}  // namespace
+
 struct moe_walk {
   uint8_t* ring = nullptr;
   int n_slots = 0;
@@ -128,6 +190,7 @@ struct moe_walk {
   std::vector<Op> ops;
   std::vector<uint8_t> streamed;
   std::vector<int32_t> slot_of, tile_first;
+  std::unique_ptr<HostShare> share;  // the CPU share, when configured
 };
 
 namespace {
@@ -144,6 +207,7 @@ void release(moe_walk* w) {
   if (w->routed) (void)hipEventDestroy(w->routed);
   if (w->copy) (void)hipStreamDestroy(w->copy);
   if (w->host) (void)hipHostFree(w->host);
+  free_host_share(w->share.get());
   delete w;
 }
 
@@ -178,6 +242,55 @@ int moe_walk_create(void* ring, int n_slots, size_t slot_stride, moe_walk** walk
 
 int moe_walk_destroy(moe_walk* walk) {
   if (walk) release(walk);
+  return MOE_OK;
+}
+
+int moe_walk_cpu_share(moe_walk* walk, double share, int max_tokens, int threads, int max_T,
+                       int H, int max_rows) {
+  if (!walk || !(share <= 1.0) || max_tokens < 0 || threads < 0) return MOE_EINVAL;
+  if (share == 0.0) {
+    free_host_share(walk->share.get());
+    walk->share.reset();
+    return MOE_OK;
+  }
+  if (max_T < 1 || H < 128 || H % 128 != 0 || max_rows < 1 ||
+      (long long)max_T * MOE_MAX_K > (1LL << 30) || (long long)max_rows * H > (1LL << 40))
+    return MOE_EINVAL;
+  std::unique_ptr<HostShare> hs(new (std::nothrow) HostShare);
+  if (!hs) return MOE_EHIP;
+  hs->share = share < 0 ? -1.0 : share;
+  hs->cur = share < 0 ? 0.25 : share;
+  hs->max_tokens = max_tokens;
+  hs->T_max = max_T;
+  hs->H = H;
+  hs->rows_max = max_rows;
+  if (threads == 0) threads = std::max(1u, std::thread::hardware_concurrency());
+  const size_t xb = (size_t)max_T * H * 4, rb = (size_t)max_rows * H * 4;
+  bool ok = hipHostMalloc(reinterpret_cast<void**>(&hs->h_x), xb, hipHostMallocDefault) ==
+                hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&hs->h_src), (size_t)max_T * MOE_MAX_K * 4,
+                          hipHostMallocDefault) == hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&hs->h_rows), rb, hipHostMallocDefault) ==
+                hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&hs->h_dst), (size_t)max_rows * 4,
+                          hipHostMallocDefault) == hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&hs->h_skip), kMaxE, hipHostMallocDefault) ==
+                hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&hs->d_rows), rb) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&hs->d_dst), (size_t)max_rows * 4) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&hs->d_skip), kMaxE) == hipSuccess &&
+            hipEventCreate(&hs->t0) == hipSuccess && hipEventCreate(&hs->t1) == hipSuccess;
+  if (ok) {
+    hs->pool.reset(new (std::nothrow) CpuPool(threads));
+    ok = hs->pool != nullptr;
+    hs->scratch.resize(threads);
+  }
+  if (!ok) {
+    free_host_share(hs.get());
+    return MOE_EHIP;
+  }
+  free_host_share(walk->share.get());
+  walk->share = std::move(hs);
   return MOE_OK;
 }
 
@@ -216,6 +329,8 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
   if (rc != MOE_OK) return rc;
   if (walk->stride < eb) return MOE_EINVAL;
   moe_walk& w = *walk;
+  HostShare* hs = w.share.get();
+  if (hs && (T > hs->T_max || H != hs->H)) return MOE_EINVAL;
   w.streamed.assign(E, 0);
   for (int e = 0; e < E; ++e) {
     if (resident[e] != nullptr) continue;
@@ -238,12 +353,59 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
       !ok(hipMemcpyAsync(h_counts, mo.counts, (size_t)E * 4, hipMemcpyDeviceToHost, s)) ||
       !ok(hipMemcpyAsync(h_order, mo.order, (size_t)E * 4, hipMemcpyDeviceToHost, s)) ||
       !ok(hipMemcpyAsync(h_nact, mo.n_active, 4, hipMemcpyDeviceToHost, s)) ||
+      (hs && !ok(hipMemcpyAsync(hs->h_x, x, (size_t)T * H * 4, hipMemcpyDeviceToHost, s))) ||
+      (hs && !ok(hipMemcpyAsync(hs->h_src, mo.src, (size_t)T * K * 4, hipMemcpyDeviceToHost,
+                                s))) ||
       !ok(hipEventRecord(w.routed, s)) ||
       !ok(launch_quantize(x, T, H, K, mo.slot, mo.src, act_mode_bits(wtype), base + L.q8x, s)) ||
       !ok(hipEventSynchronize(w.routed)))
     return MOE_EHIP;
   ++w.stats[kStSyncs];
   const int n_active = *h_nact;
+
+  // The host's share ("#1282 prefill: STRATA_PREFILL_CPU_SHARE=auto ...", "What it does"): the
+  // streamed experts routed by at most max_tokens tokens, fewest first, share x the streamed
+  // experts of this call; automatic: share = g / (c + g) from the last measured GPU time per
+  // streamed expert (g, events of the previous call, complete by this sync) and host time per
+  // expert (c), where both sides end together.
+  std::vector<int> host_experts;
+  std::vector<int64_t> off;           // expert e's first row (the maps' offsets, on the host)
+  int host_rows = 0, n_streamed = 0;
+  double share_now = 0;
+  if (hs) {
+    if (hs->timed && hs->timed_experts > 0) {
+      float ms = 0;
+      if (hipEventElapsedTime(&ms, hs->t0, hs->t1) == hipSuccess && ms > 0)
+        hs->gpu_ns = ms * 1e6 / hs->timed_experts;
+    }
+    hs->timed = false;
+    if (hs->share < 0 && hs->gpu_ns > 0 && hs->host_ns > 0)
+      hs->cur = hs->gpu_ns / (hs->gpu_ns + hs->host_ns);
+    share_now = hs->share < 0 ? hs->cur : hs->share;
+    std::vector<int> cand;
+    for (int j = 0; j < n_active; ++j) {
+      const int e = h_order[j];
+      if (e < 0 || e >= E) return MOE_EHIP;  // inconsistent device maps
+      if (w.streamed[e] != kStreamed) continue;
+      ++n_streamed;
+      if (hs->max_tokens <= 0 || h_counts[e] <= hs->max_tokens) cand.push_back(e);
+    }
+    std::sort(cand.begin(), cand.end(), [&](int a, int b) {
+      return h_counts[a] != h_counts[b] ? h_counts[a] < h_counts[b] : a < b;
+    });
+    const int want = (int)(share_now * n_streamed + 0.5);
+    for (int e : cand) {
+      if ((int)host_experts.size() >= want) break;
+      if (host_rows + h_counts[e] > hs->rows_max) break;
+      w.streamed[e] = kHost;
+      host_experts.push_back(e);
+      host_rows += h_counts[e];
+    }
+    off.assign(E, 0);
+    for (int e = 1; e < E; ++e) off[e] = off[e - 1] + h_counts[e - 1];
+  }
+  const int n_host = (int)host_experts.size();
+
   const int n = plan(h_counts, h_order, n_active, E, ring_start, w.streamed.data(), group_size,
                      w.n_slots, flags, w.used_of.data(), &w.cursor, &w.next_event, w.ops);
   if (n < 0) return MOE_EHIP;  // the device maps are inconsistent: not a caller error
@@ -276,6 +438,39 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
   dn.out = base + L.dm;
 
   const uint8_t* arena = static_cast<const uint8_t*>(host_arena);
+  // the host's experts: the MMQs skip their tiles; the pool computes their rows meanwhile
+  struct PoolJoin {  // the pool's jobs read the arena and the staging buffers: join on any exit
+    CpuPool* pool = nullptr;
+    ~PoolJoin() {
+      if (pool) pool->wait();
+    }
+  } join;
+  std::vector<int> stage_first(n_host + 1, 0);  // the expert's first staged row
+  std::chrono::steady_clock::time_point host_t0;
+  if (hs) {
+    for (int e = 0; e < E; ++e) hs->h_skip[e] = w.streamed[e] == kHost ? 1 : 0;
+    if (!ok(hipMemcpyAsync(hs->d_skip, hs->h_skip, (size_t)E, hipMemcpyHostToDevice, s)) ||
+        !ok(hipEventRecord(hs->t0, s)))
+      return MOE_EHIP;
+    gu.skip = dn.skip = hs->d_skip;
+    for (int j = 0; j < n_host; ++j) stage_first[j + 1] = stage_first[j] + h_counts[host_experts[j]];
+    if (n_host > 0) {
+      host_t0 = std::chrono::steady_clock::now();
+      hs->pool->start(n_host, [&, hs](int j, int worker) {
+        const int e = host_experts[j];
+        const int cnt = h_counts[e], first = stage_first[j];
+        std::vector<const float*> xr(cnt);
+        for (int i = 0; i < cnt; ++i) {
+          const int32_t r = (int32_t)(off[e] + i);
+          xr[i] = hs->h_x + (size_t)(hs->h_src[r] / K) * H;
+          hs->h_dst[first + i] = r;
+        }
+        cpu_expert_rows(wtype, H, F, arena + host_off[e], xr.data(), cnt,
+                        hs->h_rows + (size_t)first * H, hs->scratch[worker]);
+      });
+      join.pool = hs->pool.get();
+    }
+  }
   const size_t nops = w.ops.size();
   for (size_t k = 0; k < nops; ++k) {
     const int32_t* v = w.ops[k].v;
@@ -337,10 +532,49 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
       w.stats[kStMmq] += 2;
     }
   }
+  if (hs) {
+    if (!ok(hipEventRecord(hs->t1, s))) return MOE_EHIP;
+    hs->timed_experts = n_streamed - n_host;
+    hs->timed = hs->timed_experts > 0;
+    if (n_host > 0) {
+      join.pool = nullptr;
+      hs->pool->wait();
+      const double ns = std::chrono::duration<double, std::nano>(
+                            std::chrono::steady_clock::now() - host_t0).count();
+      hs->host_ns = ns / n_host;
+      w.stats[kStHostUs] += (int64_t)(ns / 1e3);
+      if (!ok(hipMemcpyAsync(hs->d_rows, hs->h_rows, (size_t)host_rows * H * 4,
+                             hipMemcpyHostToDevice, s)) ||
+          !ok(hipMemcpyAsync(hs->d_dst, hs->h_dst, (size_t)host_rows * 4, hipMemcpyHostToDevice,
+                             s)) ||
+          !ok(launch_scatter_rows(hs->d_rows, hs->d_dst, host_rows, H,
+                                  reinterpret_cast<float*>(base + L.dm), s)))
+        return MOE_EHIP;
+    }
+    w.stats[kStHostExperts] += n_host;
+    w.stats[kStHostRows] += host_rows;
+    w.stats[kStSharePpm] = (int64_t)(share_now * 1e6 + 0.5);
+    w.stats[kStGpuNs] = (int64_t)hs->gpu_ns;
+    w.stats[kStHostNs] = (int64_t)hs->host_ns;
+  }
   if (!ok(launch_combine(reinterpret_cast<const float*>(base + L.dm), mo.slot, topk_w, T, K, H,
                          out, s)))
     return MOE_EHIP;
   return MOE_OK;
 }
+
+int moe_cpu_expert_rows(int wtype, int H, int F, const void* expert, const float* x, int n_rows,
+                        float* out) {
+  if (!expert || !x || !out || n_rows < 1) return MOE_EINVAL;
+  if (!valid_wtype(wtype)) return MOE_EUNSUPPORTED;
+  if (H < 128 || H % 128 != 0 || F < 128 || F % 128 != 0) return MOE_EUNSUPPORTED;
+  std::vector<const float*> xr(n_rows);
+  for (int r = 0; r < n_rows; ++r) xr[r] = x + (size_t)r * H;
+  CpuScratch sc;
+  cpu_expert_rows(wtype, H, F, static_cast<const uint8_t*>(expert), xr.data(), n_rows, out, sc);
+  return MOE_OK;
+}
+
+const char* moe_cpu_share_isa(void) { return cpu_share_isa(); }
 
 }  // extern "C"

@@ -198,3 +198,86 @@ def test_streamed_host_validation():
     assert abi.raw_prefill_layer_streamed(**args(group_size=17)) == -1
     assert s.walk.stats()["routing_syncs"] == 0              # nothing was enqueued
     s.walk.close()
+
+
+SHARE_CASES = [
+    # name, T, H, F, E, K, wtype, zipf
+    ("share_q8_0", 96, 256, 128, 40, 4, synth.Q8_0, 0.7),
+    ("share_q4_1", 150, 512, 256, 48, 3, synth.Q4_1, None),
+    ("share_d4", 64, 256, 128, 24, 2, synth.Q8_0_D4, 1.1),
+]
+
+
+@pytest.mark.parametrize("case", SHARE_CASES, ids=[c[0] for c in SHARE_CASES])
+def test_streamed_walk_cpu_share(orc, case):
+    """The CPU share ("#1282 prefill: STRATA_PREFILL_CPU_SHARE=auto hands a small chunk's
+    least-routed experts to the idle CPU pool", "What it does"): the host takes the least-routed
+    streamed experts (at most max_tokens tokens each, fewest first), the GPU neither copies nor
+    gathers them, the combine weights their rows.  The output is within the layer's tolerance of
+    the oracle; a token none of whose routes went to the host equals the resident layer bit for
+    bit (its rows are the GPU's)."""
+    name, T, H, F, E, K, wtype, zipf = case
+    c = synth.make_case(name, T=T, H=H, F=F, E=E, K=K, wtype=wtype,
+                        seed=zlib.crc32(name.encode()) % 10000, zipf=zipf, zero_tokens=(5,))
+    idx, w = orc.route_topk(c.logits, K)
+    want = orc.prefill_layer(c.x, idx, w, wtype, c.pool, c.expert_off, F, E)
+    m = orc.build_maps(idx, E, c.ring_start)
+    for share, max_tok, n_slots, res in [(0.5, 0, 8, "none"), (1.0, 6, 3, "third"),
+                                         (-1.0, 0, 96, "none")]:
+        s = Streamed(c, n_slots)
+        s.walk.cpu_share(share, max_tok, 4, T, H, T * K)
+        ref = s.reference(c.x, idx, w, 16, c.ring_start)
+        mask = _mask(res, E)
+        prev = None
+        for call in range(2 if share < 0 else 1):
+            st0 = s.walk.stats()
+            got = s.run(c.x, idx, w, mask, 16, c.ring_start, 0)
+            last = s.walk.stats()       # share_ppm and the two rates describe the last call
+            st = {k: v - st0[k] for k, v in last.items()}
+            assert rel_err(got, want) <= TOL, (share, call)
+            assert not got[5].any()
+            streamed_routed = [e for e in range(E) if m["counts"][e] > 0 and not mask[e]]
+            counts = m["counts"]
+            order = sorted(streamed_routed, key=lambda e: (counts[e], e))
+            eligible = [e for e in order if max_tok == 0 or counts[e] <= max_tok]
+            # the host takes share x the streamed experts (the share this call used: fixed, or
+            # 0.25 on an automatic walk's first call and g / (c + g) after), least-routed first
+            used = last["share_ppm"] / 1e6
+            if share > 0:
+                assert used == share
+            elif call == 0:
+                assert used == 0.25
+            n_host = min(len(eligible), int(used * len(streamed_routed) + 0.5))
+            assert st["host_experts"] == n_host, (share, call, st)
+            if share > 0 or call == 0:
+                assert n_host > 0
+            assert st["copies"] == len(streamed_routed) - n_host
+            assert st["host_rows"] == int(sum(counts[e] for e in eligible[:n_host]))
+            # tokens not routed to any of the host's experts are the GPU's alone
+            host = set(eligible[:n_host])
+            clean = ~np.isin(idx, list(host)).any(axis=1)
+            assert clean.sum() > 0
+            assert np.array_equal(got[clean], ref[clean]), (share, call)
+            if share < 0 and call == 1:  # the share came from the rates measured by call 0:
+                g = last["gpu_ns_per_expert"]          # the GPU's (its events, read now)
+                c = prev["host_ns_per_expert"]         # and the host's (timed in call 0)
+                assert g > 0 and c > 0
+                assert abs(used - g / (g + c)) < 1e-5
+            prev = last
+        s.walk.close()
+
+
+def test_streamed_walk_cpu_share_rejects_shapes_outside_its_buffers(orc):
+    c = synth.make_case("share_val", T=40, H=256, F=128, E=12, K=2, wtype=synth.Q8_0, seed=9)
+    s = Streamed(c, 4)
+    s.walk.cpu_share(0.5, 0, 2, 20, 256, 40)       # T above the share's capacity
+    idx, w = orc.route_topk(c.logits, c.K)
+    out = torch.empty((c.T, c.H), dtype=torch.float32, device="cuda")
+    rc = abi.raw_prefill_layer_streamed(s.walk, dev(c.x), dev(idx), dev(w), c.wtype, s.arena,
+                                        c.expert_off, [0] * c.E, c.F, c.E, 16, 0, 0, s.ws, out)
+    assert rc == -1
+    s.walk.cpu_share(0.0, 0, 0, 0, 0, 0)           # off: the call runs on the GPU alone
+    assert abi.raw_prefill_layer_streamed(s.walk, dev(c.x), dev(idx), dev(w), c.wtype, s.arena,
+                                          c.expert_off, [0] * c.E, c.F, c.E, 16, 0, 0, s.ws,
+                                          out) == 0
+    s.walk.close()

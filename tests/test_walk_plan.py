@@ -7,7 +7,10 @@ released by one event" sets in "What changes":
   - one wait per batch, on the batch's last copy (the copy stream is in order);
   - one event per batch, releasing every ring slot the batch read; a copy that refills a slot
     waits on used[used_of[slot]], and an event recorded again later only delays that copy;
-  - a slot is never refilled before the batch that reads it has been launched.
+  - a slot is never refilled before the batch that reads it has been launched;
+and, with the CPU share ("#1282 prefill: STRATA_PREFILL_CPU_SHARE=auto ...", "What it does":
+the host takes some streamed experts and the GPU the rest), an expert the host computes is
+neither copied nor gathered, and no batch spans its position.
 
 The checker below replays the op list the library returns with its own model of the two streams
 and the events; it shares nothing with the planner but the op encoding of include/moe_prefill.h.
@@ -52,6 +55,7 @@ def check_call(sim, ops, counts, ring_start, streamed, G, flags):
         if kind == OP_COPY:
             pos, e, s, wait = (int(v) for v in op[1:5])
             assert 0 <= pos < n_active and routed[pos] == e, f"op {k}: copy of a wrong expert"
+            assert streamed[e] != 2, f"op {k}: copy of an expert the host computes"
             assert streamed[e], f"op {k}: copy of a resident expert"
             assert 0 <= s < sim.n_slots, f"op {k}: slot out of range"
             assert s not in open_slots, f"op {k}: slot {s} refilled before its batch was launched"
@@ -76,6 +80,7 @@ def check_call(sim, ops, counts, ring_start, streamed, G, flags):
                 assert not gathered[p], f"op {k}: position {p} gathered twice"
                 gathered[p] = True
                 e = routed[p]
+                assert streamed[e] != 2, f"op {k}: gather of an expert the host computes"
                 if streamed[e]:
                     s = copy_of_pos.get(p)
                     assert s is not None, f"op {k}: streamed position {p} has no copy"
@@ -101,12 +106,14 @@ def check_call(sim, ops, counts, ring_start, streamed, G, flags):
         elif kind == OP_MMQ:
             g, first, n = (int(v) for v in op[1:4])
             assert first == g * G and n == min(G, n_active - first), f"op {k}: wrong MMQ group"
-            assert all(gathered[first:first + n]), f"op {k}: MMQ before its group was gathered"
+            assert all(gathered[p] or streamed[routed[p]] == 2 for p in range(first, first + n)), \
+                f"op {k}: MMQ before its group was gathered"
             assert not mmq_groups or mmq_groups[-1] == g - 1
             mmq_groups.append(g)
         else:
             raise AssertionError(f"op {k}: unknown kind {kind}")
-    assert all(gathered), "a routed expert was never gathered"
+    host = [streamed[e] == 2 for e in routed]
+    assert all(g or h for g, h in zip(gathered, host)), "a routed expert was never gathered"
     assert mmq_groups == list(range((n_active + G - 1) // G)), "a group's MMQ is missing"
     assert not open_slots
     return batches
@@ -263,3 +270,59 @@ def test_plan_rejects_inconsistent_inputs():
     assert abi.walk_plan(counts, [0, 2], 2, 0, ones, 4, 2, 0, st(), max_ops=2)[0] == -3
     n, ops, _ = abi.walk_plan(counts, [2, 0], 2, 2, ones, 4, 2, 0, st())       # ring from 2
     assert n == 4 and [int(o[2]) for o in ops if o[0] == OP_COPY] == [2, 0]
+
+
+@pytest.mark.parametrize("E", [7, 64, 512])
+@pytest.mark.parametrize("G", [1, 3, 16])
+@pytest.mark.parametrize("n_slots", [1, 5, 96])
+def test_schedule_with_host_experts(E, G, n_slots):
+    """Some streamed experts computed by the host (state 2), mixed with resident and streamed
+    ones, over three calls that carry the ring's state."""
+    rng = np.random.default_rng(E * 77 + G * 7 + n_slots)
+    sim = Sim(n_slots)
+    state = None
+    for call in range(3):
+        counts = _case(rng, E, zero_frac=[0.0, 0.3, 0.6][call])
+        ring_start = int(rng.integers(E))
+        streamed = (rng.random(E) < 0.8).astype(np.uint8)
+        streamed[(streamed == 1) & (rng.random(E) < [0.5, 0.1, 0.9][call])] = 2
+        ops, state = _plan(counts, ring_start, streamed, G, n_slots, 0, state)
+        batches = check_call(sim, ops, counts, ring_start, streamed, G, 0)
+        ring = [(ring_start + i) % E for i in range(E)]
+        routed = [e for e in ring if counts[e] > 0]
+        for first, n, _ in batches:              # no batch spans a host expert's position
+            for p in range(first, first + n):
+                assert streamed[routed[p]] != 2
+
+
+def test_host_expert_splits_the_batch():
+    # ring 0..7 all routed, group 4, expert 2 computed by the host: batches (0,2) and (3,1)
+    counts = np.full(8, 2, np.int32)
+    streamed = np.ones(8, np.uint8)
+    streamed[2] = 2
+    ops, _ = _plan(counts, 0, streamed, 4, 16, 0, None)
+    gathers = [(int(o[1]), int(o[2]), int(o[5])) for o in ops if o[0] == OP_GATHER]
+    assert gathers == [(0, 2, 4), (3, 1, 0), (4, 4, 0)]
+    assert [int(o[2]) for o in ops if o[0] == OP_COPY] == [0, 1, 3, 4, 5, 6, 7]
+    assert [(int(o[1]), int(o[2]), int(o[3])) for o in ops if o[0] == OP_MMQ] == [(0, 0, 4),
+                                                                                   (1, 4, 4)]
+    # a whole group computed by the host: no gather for it, its MMQ record still comes
+    streamed[4:8] = 2
+    ops, _ = _plan(counts, 0, streamed, 4, 16, 0, None)
+    assert [(int(o[1]), int(o[2])) for o in ops if o[0] == OP_GATHER] == [(0, 2), (3, 1)]
+    assert [int(o[1]) for o in ops if o[0] == OP_MMQ] == [0, 1]
+
+
+def test_checker_catches_a_gathered_host_expert():
+    counts = np.full(8, 2, np.int32)
+    streamed = np.ones(8, np.uint8)
+    ops, _ = _plan(counts, 0, streamed, 4, 16, 0, None)     # planned as all streamed
+    streamed[2] = 2                                          # but checked as host-computed
+    with pytest.raises(AssertionError):
+        check_call(Sim(16), ops, counts, 0, streamed, 4, 0)
+
+
+def test_plan_rejects_an_unknown_expert_state():
+    counts = np.array([2, 0, 3], np.int32)
+    st = {"used_of": np.full(2, -1, np.int32), "cursor": 0, "next_event": 0}
+    assert abi.walk_plan(counts, [0, 2], 2, 0, np.array([1, 1, 3], np.uint8), 4, 2, 0, st)[0] == -1
