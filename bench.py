@@ -388,7 +388,7 @@ def quant_ab(args, dev):
         row = {"T": T, "rows": R}
         for cache in ("warm", "cold"):
             for mode_name, mode in (("gather", abi.QUANT_PER_ROW), ("scatter", 0)):
-                for _ in range(3):
+                for _ in range(args.warmup):
                     abi.quantize_scatter_q8_1(x, K, m["slot"], m["src"], mode, q8)
                 ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                       for _ in range(args.steps)]
@@ -416,7 +416,7 @@ def quant_ab(args, dev):
         "unit": "x",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": 3,
+        "warmup": args.warmup,
         "ms_per_step": results[-1]["cold_scatter_ms"],
         "higher_is_better": True,
         "scaling": "weak",

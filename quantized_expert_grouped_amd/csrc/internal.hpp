@@ -106,7 +106,7 @@ struct MmqProblem {
   const int32_t* n_tiles;
   int max_tiles;
   int tile_count;
-  int n_tiles_n;          // weight-row tiles per m-tile (set by the launcher)
+  int n_tiles_n;          // workgroups per m-tile (set by the launcher)
   int32_t* misaligned;    // layer form, packed pool: count of m-tiles skipped (or nullptr)
   const uint8_t* skip;    // layer form: skip[e] != 0 -> expert e's tiles are not computed
                           // (the host computes them), or nullptr
@@ -120,7 +120,8 @@ hipError_t launch_mmq(const MmqProblem& p, hipStream_t s);
 constexpr long long kMaxGridX = 0x7fffffffLL;
 inline long long mmq_layer_workgroups(int n_out_gu, int n_out_dn, int max_tiles) {
   const long long a = (long long)(n_out_gu / 64) * max_tiles;    // gate/up: 64 features a tile
-  const long long b = (long long)(n_out_dn / 128) * max_tiles;   // down: 128 output columns
+  // down: 128 output columns a tile, up to 4 tiles a workgroup
+  const long long b = (long long)((n_out_dn / 128 + 3) / 4) * max_tiles;
   return a > b ? a : b;
 }
 

@@ -20,7 +20,8 @@
 // sequence, so results do not depend on the tiling, the group size, the ring start or the row's
 // place in its tile.
 //
-// Workgroup: 64 activation rows (one m-tile of one expert) x 128 weight rows, 4 wavefronts.
+// Workgroup: 64 activation rows (one m-tile of one expert) x 128 weight rows, 4 wavefronts; the
+// fp32-output kernel's workgroup goes on through up to 4 such weight-row tiles (n-tiles) in turn.
 // Wavefront (wr, wc) owns rows 32*wr.. and two 32-row column tiles of the weights:
 //   MOE_EPI_SWIGLU_Q8_1: gate features f0+32wc.. and the up rows of the same features, so
 //     h = silu(g) * u is formed in registers and requantised along F across the 32 lanes that
@@ -83,9 +84,21 @@ struct alignas(16) StageBuf {
 // LDS stage buffers per workgroup: two (19.5 KB for Q4_1, 26.6 KB for Q8_0; one stage in flight
 // ahead of the MFMAs), so that three workgroups fit in a CU's 160 KB and in 168 VGPRs: three
 // wavefronts per SIMD hide each other's waits better than deeper prefetch does (a ring of four,
-// or three, at two workgroups per CU was 5-9% slower).  The raw block-dot epilogue and the
-// per-group kernel stay at two workgroups per CU (they would spill at three).
+// or three, at two workgroups per CU was 5-9% slower).  Q4_1's gate/up kernel runs four (its
+// ring fits four times in LDS, and it fits 128 VGPRs when each column tile's MFMAs and
+// convert + fma run in turn; measured 3% faster at T = 8,192); Q4_1's down kernel does not fit
+// 128 VGPRs without spills and stays at three.  The raw block-dot epilogue and the per-group
+// kernel stay at two workgroups per CU (they would spill at three).
 constexpr int kWgPerCu = 3;
+template <int WT, int EPI>
+constexpr int wg_per_cu() {
+  return EPI == 2 ? 2 : (WT == 1 && EPI == 1 ? 4 : kWgPerCu);
+}
+
+// The fp32-output (down) kernel's workgroup sweeps up to kSweep consecutive n-tiles of its m-tile
+// through one ring: its short reduction (k_in = F, a few stages) would otherwise pay a ring fill
+// and an output drain per n-tile (measured at T = 8,192 / 32,768: down -4% / -9%).
+constexpr int kSweep = 4;
 
 template <int WT>
 struct Ring {
@@ -214,7 +227,7 @@ __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
 template <int WT, int EPI, int NG = 4>
 __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
                                          const MmqProblem& p, const uint8_t* W, int row0,
-                                         int nrows, int ntile) {
+                                         int nrows, int ntile, int nsweep = 1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
@@ -245,20 +258,14 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   const v16i izero = {0};
   const v16f fzero = {0.0f};
 
-  auto issue = [&](StageBuf<WT>& buf, int t) {
-    issue_stage<WT>(buf, plan, abase + (size_t)t * kARow, W + (size_t)t * 64 * Geo<WT>::kBRow);
+  // stage t of the sweep's n-tile j (EPI 0: n-tile j's weights start 2j 64-row tiles later)
+  auto issue = [&](StageBuf<WT>& buf, int j, int t) {
+    issue_stage<WT>(buf, plan, abase + (size_t)t * kARow,
+                    W + (size_t)j * 2 * tile_bytes + (size_t)t * 64 * Geo<WT>::kBRow);
   };
 
-  // One stage: wait until this wavefront's loads of stage s are done and, at the barrier, every
-  // wavefront's (which also means every wavefront is done with stage s-1, whose buffer `fill`
-  // then receives stage s + 1), then its MFMAs.  The two buffers are distinct LDS objects used
-  // with fixed roles per unrolled step, so the compiler can tell the reads of one from the
-  // loads into the other and keeps the loads in flight.
-  auto step = [&](int s, const StageBuf<WT>& cur, StageBuf<WT>& fill) {
-    __builtin_amdgcn_s_waitcnt(vm_imm(0));
-    __builtin_amdgcn_s_barrier();
-    if (s + 1 < nstages) issue(fill, s + 1);
-    if (!live) return;
+  // The MFMAs of stage s from LDS buffer `cur` into the accumulators.
+  auto math = [&](int s, const StageBuf<WT>& cur) {
     const uint8_t* arow = cur.a + (32 * wr + l32) * kARow;
     const uint8_t* brow0 = cur.b + (32 * ct0 + l32) * Geo<WT>::kBRow;
     const uint8_t* brow1 = cur.b + (32 * ct1 + l32) * Geo<WT>::kBRow;
@@ -320,6 +327,24 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
         za[b >> 1] = (b & 1) ? (int)((uint32_t)hx[b] << 16) : (int)((uint32_t)hx[b] & 0xffffu);
       }
       const v8h sx = __builtin_bit_cast(v8h, za);
+      if (WT == 1 && EPI == 1) {  // one column tile after the other (fits 128 VGPRs)
+        {
+          const v16i I0 =
+              __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x0), izero, 0, 0, 0);
+          const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4 * NG; ++i) acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          const v16i I1 =
+              __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x1), izero, 0, 0, 0);
+          const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw1, fzero, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4 * NG; ++i) acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
+        }
+        continue;
+      }
       const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x0), izero, 0, 0, 0);
       const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
       const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x1), izero, 0, 0, 0);
@@ -347,37 +372,83 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
     }
   };
 
+  // EPI 0: n-tile j's fp32 rows (the doubled scales' factor 2 removed, exactly), then the
+  // accumulators cleared for the next n-tile.  A uniform base and one 32-bit lane offset
+  // (64 rows x n_out floats stay below 2^31 bytes), computed at the store rather than hoisted
+  // out of the stage loop, where they would hold registers.
+  auto store_f32 = [&](int j) {
+    float* ob = reinterpret_cast<float*>(p.out) + (size_t)row0 * p.n_out + n0 + j * kRowsN;
+    uint32_t off = (uint32_t)((32 * wr + 4 * half) * p.n_out + l32);
+    asm volatile("" : "+v"(off));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
+      if (row < nrows) {
+        ob[off + 32 * ct0] = 0.5f * acc0[i];
+        ob[off + 32 * ct1] = 0.5f * acc1[i];
+      }
+      off += (uint32_t)p.n_out * ((i & 3) == 3 ? 5u : 1u);
+      acc0[i] = 0.0f;
+      acc1[i] = 0.0f;
+    }
+  };
+
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the previous tile
   __builtin_amdgcn_s_barrier();        // ... and every other wave's, before the ring refills
-  issue(L0, 0);
-  for (int s0 = 0; s0 < nstages; s0 += 2) {  // stage s + 1 goes into the other buffer
+  issue(L0, 0, 0);
+  if (EPI == 0) {
+    // Sweep: the step computing stage cs of n-tile cj.  Each step waits until this wavefront's
+    // loads of its stage are done and, at the barrier, every wavefront's (which also means every
+    // wavefront is done with the previous stage, whose buffer `fill` then receives the next),
+    // then its MFMAs.  An n-tile finished by the previous step is stored first, before this
+    // step's loads are issued: the next wait (vector memory counts stores and loads alike) then
+    // finds the stores done as well, after a whole stage of MFMAs.
+    int cj = 0, cs = 0;
+    auto step = [&](const StageBuf<WT>& cur, StageBuf<WT>& fill) {
+      __builtin_amdgcn_s_waitcnt(vm_imm(0));
+      __builtin_amdgcn_s_barrier();
+      if (cs == 0 && cj > 0 && live) store_f32(cj - 1);
+      const int s = cs;
+      int nj = cj, ns = cs + 1;
+      if (ns == nstages) {
+        ns = 0;
+        ++nj;
+      }
+      if (nj < nsweep) issue(fill, nj, ns);
+      cj = nj;
+      cs = ns;
+      if (live) math(s, cur);
+    };
+    const int total = nstages * nsweep;
+    for (int t = 0; t < total; t += 2) {  // stage t + 1 goes into the other buffer
+      step(L0, L1);
+      if (t + 1 < total) step(L1, L0);
+    }
+    if (live) store_f32(nsweep - 1);
+    return;
+  }
+  // One n-tile: the same steps without the sweep's bookkeeping.  The two buffers are distinct
+  // LDS objects used with fixed roles per unrolled step, so the compiler can tell the reads of
+  // one from the loads into the other and keeps the loads in flight.
+  auto step = [&](int s, const StageBuf<WT>& cur, StageBuf<WT>& fill) {
+    __builtin_amdgcn_s_waitcnt(vm_imm(0));
+    __builtin_amdgcn_s_barrier();
+    if (s + 1 < nstages) issue(fill, 0, s + 1);
+    if (live) math(s, cur);
+  };
+  for (int s0 = 0; s0 < nstages; s0 += 2) {
     step(s0, L0, L1);
     if (s0 + 1 < nstages) step(s0 + 1, L1, L0);
   }
   if (EPI == 2) return;
-  if (EPI == 1) {  // every wavefront is past its last stage: the ring becomes scratch
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-  }
+  // EPI 1: every wavefront is past its last stage: the ring becomes scratch
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
   if (!live) return;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {  // remove the factor 2 of the doubled scales (exact)
     acc0[i] *= 0.5f;
     acc1[i] *= 0.5f;
-  }
-
-  if (EPI == 0) {
-    float* out = reinterpret_cast<float*>(p.out);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (row < nrows) {
-        float* o = out + (size_t)(row0 + row) * p.n_out + n0;
-        o[32 * ct0 + l32] = acc0[i];
-        o[32 * ct1 + l32] = acc1[i];
-      }
-    }
-    return;
   }
 
   // EPI == 1: h = silu(g) * u, then q8_1 along F.  A lane holds one feature of 16 rows; the
@@ -446,7 +517,7 @@ constexpr int kXcds = 8;
 
 // The launch is one-dimensional (the host keeps n-tiles x m-tiles within the grid's x limit).
 template <int WT, int EPI>
-__global__ __launch_bounds__(256, EPI == 2 ? 2 : kWgPerCu) void mmq_layer_kernel(MmqProblem p) {
+__global__ __launch_bounds__(256, (wg_per_cu<WT, EPI>())) void mmq_layer_kernel(MmqProblem p) {
   __shared__ Ring<WT> ring;
   const int ntl = p.n_tiles_n;
   const int live = ntl * (p.tile_count > 0 ? p.tile_count : *p.n_tiles);
@@ -471,18 +542,17 @@ __global__ __launch_bounds__(256, EPI == 2 ? 2 : kWgPerCu) void mmq_layer_kernel
   // padding rows (the MFMAs still cover all 32)
   const int nh = t.nrows - 32 * (wave_id() >> 1);
   const int ng = (EPI == 2 || nh <= 0 || nh >= 32) ? 4 : (nh + 7) / 8;
+  // EPI 0: the workgroup's n-tiles kSweep * (work % ntl) onwards, at most kSweep of them
+  const int nt0 = EPI == 0 ? (work % ntl) * kSweep : work % ntl;
+  const int nsw = EPI == 0 ? min(kSweep, p.n_out / kRowsN - nt0) : 1;
   if (ng == 4)
-    mmq_tile<WT, EPI, 4>(ring.buf[0], ring.buf[1], p, W, t.row0,
-                         t.nrows, work % ntl);
+    mmq_tile<WT, EPI, 4>(ring.buf[0], ring.buf[1], p, W, t.row0, t.nrows, nt0, nsw);
   else if (ng == 3)
-    mmq_tile<WT, EPI, 3>(ring.buf[0], ring.buf[1], p, W, t.row0,
-                         t.nrows, work % ntl);
+    mmq_tile<WT, EPI, 3>(ring.buf[0], ring.buf[1], p, W, t.row0, t.nrows, nt0, nsw);
   else if (ng == 2)
-    mmq_tile<WT, EPI, 2>(ring.buf[0], ring.buf[1], p, W, t.row0,
-                         t.nrows, work % ntl);
+    mmq_tile<WT, EPI, 2>(ring.buf[0], ring.buf[1], p, W, t.row0, t.nrows, nt0, nsw);
   else
-    mmq_tile<WT, EPI, 1>(ring.buf[0], ring.buf[1], p, W, t.row0,
-                         t.nrows, work % ntl);
+    mmq_tile<WT, EPI, 1>(ring.buf[0], ring.buf[1], p, W, t.row0, t.nrows, nt0, nsw);
 }
 
 template <int WT, int EPI>
@@ -502,8 +572,8 @@ hipError_t launch_typed(const MmqProblem& p, hipStream_t s) {
   const int ntiles = EPI == 1 ? p.n_out / 64 : p.n_out / kRowsN;
   if (p.tiles != nullptr) {
     MmqProblem q = p;
-    q.n_tiles_n = ntiles;
-    const long long n = (long long)ntiles * (p.tile_count > 0 ? p.tile_count : p.max_tiles);
+    q.n_tiles_n = EPI == 0 ? (ntiles + kSweep - 1) / kSweep : ntiles;  // workgroups per m-tile
+    const long long n = (long long)q.n_tiles_n * (p.tile_count > 0 ? p.tile_count : p.max_tiles);
     if (n > kMaxGridX) return hipErrorInvalidConfiguration;   // refused by the ABI's checks
     mmq_layer_kernel<WT, EPI><<<dim3((unsigned)n), 256, 0, s>>>(q);
   } else {

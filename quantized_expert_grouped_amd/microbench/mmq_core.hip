@@ -20,6 +20,12 @@
 //                    sets), one MFMA then 16 VALU ops
 //   i8 into AGPRs    the int8 MFMAs write accumulation registers (inline asm), each element is
 //                    read back before its convert
+//   VALU scales      no f16 MFMA: the scale products come from the VALU, S = dx * dw exactly with
+//                    one v_fma_mix_f32 (fp16 operands, zero addend) per element; the 16 weight
+//                    scales of a lane's 16 output elements are read from LDS every block (two
+//                    16-byte reads per tile, one address per half-wavefront), dx is one fp16 per
+//                    lane.  The orientation this needs: lanes = activation rows, registers =
+//                    weight rows.
 // each at 2, 3 and 4 wavefronts per SIMD (set by the LDS a workgroup reserves).
 #include <hip/hip_runtime.h>
 #include <stdio.h>
@@ -113,10 +119,10 @@ double rate(int ncu, const int* din, float* dout, double macs, int per_iter, dou
 }
 
 // ---- part 2 ------------------------------------------------------------------------------------
-enum { M_FULL, M_NOCVT, M_NOF16, M_NOI8, M_MFMA, M_VALU, M_BIAS, M_PIPE, M_AGPR, M_COUNT };
+enum { M_FULL, M_NOCVT, M_NOF16, M_NOI8, M_MFMA, M_VALU, M_BIAS, M_PIPE, M_AGPR, M_VS, M_COUNT };
 static const char* kMixName[M_COUNT] = {"full", "no convert", "no f16 MFMA", "no i8 MFMA",
                                         "MFMAs only", "VALU only", "bias + add", "pipelined",
-                                        "i8 into AGPRs"};
+                                        "i8 into AGPRs", "VALU scales"};
 
 template <int M, int W>
 __global__ __launch_bounds__(256, W) void mix_kernel(const int* __restrict__ in,
@@ -149,7 +155,50 @@ __global__ __launch_bounds__(256, W) void mix_kernel(const int* __restrict__ in,
     b1[2] += blk;
     sa[0] = (sa[0] + 1) & 0x3fff;
   };
-  if (M == M_PIPE) {
+  if (M == M_VS) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    // 8 blocks x 2 tiles x 2 half-wavefronts x 16 fp16 weight scales in LDS (as packed pairs)
+    uint32_t* ws = reinterpret_cast<uint32_t*>(lds_reserve);
+    for (int i = threadIdx.x; i < 8 * 2 * 2 * 8; i += blockDim.x) {
+      const h2 v = {(_Float16)(1.0f + (float)(in[(2 * i) & 1023] & 1023) / 1024.0f),
+                    (_Float16)(1.0f + (float)(in[(2 * i + 1) & 1023] & 1023) / 1024.0f)};
+      ws[i] = __builtin_bit_cast(uint32_t, v);
+    }
+    __syncthreads();
+    const int half = lane >> 5;
+    for (int blk = 0; blk < nblocks; ++blk) {
+      next_operands(blk);
+      const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
+      const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
+      const _Float16 dx = __builtin_bit_cast(h2, sa[0]).x;
+      const uint32_t* w0 = ws + ((blk & 7) * 4 + half) * 8;
+      const uint32_t* w1 = w0 + 16;
+      h2 d0[8], d1[8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(w0 + 4 * j);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(w1 + 4 * j);
+        d0[4 * j] = __builtin_bit_cast(h2, x0.x);
+        d0[4 * j + 1] = __builtin_bit_cast(h2, x0.y);
+        d0[4 * j + 2] = __builtin_bit_cast(h2, x0.z);
+        d0[4 * j + 3] = __builtin_bit_cast(h2, x0.w);
+        d1[4 * j] = __builtin_bit_cast(h2, x1.x);
+        d1[4 * j + 1] = __builtin_bit_cast(h2, x1.y);
+        d1[4 * j + 2] = __builtin_bit_cast(h2, x1.z);
+        d1[4 * j + 3] = __builtin_bit_cast(h2, x1.w);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float S0 = __builtin_fmaf((float)dx, (float)(i & 1 ? d0[i >> 1].y : d0[i >> 1].x), 0.0f);
+        acc0[i] = fmaf((float)I0[i], S0, acc0[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float S1 = __builtin_fmaf((float)dx, (float)(i & 1 ? d1[i >> 1].y : d1[i >> 1].x), 0.0f);
+        acc1[i] = fmaf((float)I1[i], S1, acc1[i]);
+      }
+    }
+  } else if (M == M_PIPE) {
     v16i Ia0 = izero, Ia1 = izero, Ib0, Ib1;
     v16f Sa0 = fzero, Sa1 = fzero, Sb0, Sb1;
     auto step = [&](int blk, v16i& nI0, v16i& nI1, v16f& nS0, v16f& nS1, const v16i& I0,
@@ -311,6 +360,7 @@ int main() {
   mix_row<M_BIAS>(ncu, din, dout);
   mix_row<M_PIPE>(ncu, din, dout);
   mix_row<M_AGPR>(ncu, din, dout);
+  mix_row<M_VS>(ncu, din, dout);
   const hipError_t e = hipDeviceSynchronize();
   printf("\nstatus %s\n", hipGetErrorString(e));
   return e == hipSuccess ? 0 : 1;

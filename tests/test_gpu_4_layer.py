@@ -39,6 +39,9 @@ CASES = [
     ("ragged_d4", 301, 512, 256, 24, 4, synth.Q8_0_D4, None),
     ("three_stages", 150, 384, 384, 12, 3, synth.Q4_1, None),
     ("three_stages_q8_0", 150, 384, 384, 12, 3, synth.Q8_0, None),
+    # H = 640: five 128-column n-tiles, a down workgroup's sweep of four and one of one
+    ("five_ntiles", 211, 640, 256, 14, 3, synth.Q4_1, None),
+    ("five_ntiles_q8_0", 211, 640, 256, 14, 3, synth.Q8_0, 1.2),
 ]
 
 
