@@ -38,8 +38,15 @@ def _abs_term_bound(wtype, wmat, n_out, k_in, act, dots):
 
 
 def _d4_scale_bound(wtype, wmat, n_out, k_in, act, dots):
-    """D4 only: the kernel carries each fp32 d as fp16(d) + fp16(d - fp16(d)), within
-    max(2^-22 d, 2^-25) of d; this bounds what that moves sum_b y_b (twice, for margin)."""
+    """D4 only: what the kernel's scale arithmetic moves sum_b y_b, beyond the fp32 accumulation.
+
+    Two terms per block, each at most |I_b| * |dw_b| * max(2^-22 dx_b, 2^-25):
+      - representation: dx enters as hi + lo = fp16(dx) + fp16(dx - fp16(dx)); the remainder is
+        at most 2^-11 dx and lo rounds it to 2^-11 of itself, or to half fp16's smallest
+        subnormal (2^-25), so |dx - (hi + lo)| <= max(2^-22 dx, 2^-25);
+      - the MFMA's sum of the two exact fp32 products hi*dw + lo*dw: one rounding, at most
+        2^-24 |(hi + lo) dw| <= 2^-23 dx |dw|, within the same max.
+    Hence the factor 2."""
     if wtype != synth.Q8_0_D4:
         return 0.0
     _, d, _ = npref.unpack_matrix(wmat, n_out, k_in, wtype)
