@@ -156,19 +156,36 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "{m0}"(lds), "v"(g) : "memory");
 }
 
-template <int WT>
-__device__ __forceinline__ void issue_stage(StageBuf<WT>& S, const DmaPlan<WT>& d,
-                                            const uint8_t* abase, const uint8_t* wbase) {
-  const int wave = wave_id();
+// Wavefront W of the workgroup issues pieces W, W + 4, ... of the stage: with W a template
+// argument every piece's presence and LDS address are compile-time, so the issue is straight-line
+// code (a runtime wavefront index cost a compare and a branch per piece).
+template <int WT, int W>
+__device__ __forceinline__ void issue_stage_w(uint32_t la, uint32_t lb, const DmaPlan<WT>& d,
+                                              const uint8_t* abase, const uint8_t* wbase) {
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const int i = wave + 4 * j;
-    if (i < kAInstr) dma16(abase + d.a[j], lds_address(S.a + i * 1024));
+    const int i = W + 4 * j;
+    if (i < kAInstr) dma16(abase + d.a[j], la + i * 1024);
   }
 #pragma unroll
   for (int j = 0; j < Geo<WT>::kBPerWave; ++j) {
-    const int i = wave + 4 * j;
-    if (i < Geo<WT>::kBInstr) dma16(wbase + d.b[j], lds_address(S.b + i * 64 * 16));
+    const int i = W + 4 * j;
+    if (i < Geo<WT>::kBInstr) dma16(wbase + d.b[j], lb + i * 64 * 16);
+  }
+}
+
+template <int WT>
+__device__ __forceinline__ void issue_stage(StageBuf<WT>& S, const DmaPlan<WT>& d,
+                                            const uint8_t* abase, const uint8_t* wbase) {
+  // the buffers' LDS addresses as opaque values (folded into constants, the generic-to-LDS
+  // pointer conversion miscompiled)
+  uint32_t la = lds_address(S.a), lb = lds_address(S.b);
+  asm volatile("" : "+s"(la), "+s"(lb));
+  switch (wave_id()) {
+    case 0: issue_stage_w<WT, 0>(la, lb, d, abase, wbase); break;
+    case 1: issue_stage_w<WT, 1>(la, lb, d, abase, wbase); break;
+    case 2: issue_stage_w<WT, 2>(la, lb, d, abase, wbase); break;
+    default: issue_stage_w<WT, 3>(la, lb, d, abase, wbase); break;
   }
 }
 
