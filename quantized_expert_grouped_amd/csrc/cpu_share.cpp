@@ -7,14 +7,19 @@
 // DS4, the fp32 d for D4), then for every weight row and block b the integer dot I_b of the 32
 // weight values with the 32 activation values, y_b = dw * dx * I_b (+ mw * sx for Q4_1), summed
 // over b; h = silu(g) * u is quantised to q8_1 along F the same way and goes through the down
-// matrix.  The integer dots are exact; the fp32 sums run in SIMD lanes (8 partial dots of 4
-// products each, scaled and accumulated per lane, then added across lanes), another order than
-// the GPU's, which is why the host's rows are not bit-identical to the GPU's.
+// matrix.  The integer dots are exact; the fp32 sums run in SIMD lanes (per block 8 partial dots
+// of 4 products each, scaled by dw * dx and accumulated per lane, blocks 2i and 2i + 1 in lanes
+// 0-7 and 8-15, the lanes added at the end; Q4_1's min term as a separate 8-lane dot of m and s),
+// another order than the GPU's, which is why the host's rows are not bit-identical to the GPU's.
 //
 // The dot products use AVX-512 VNNI (vpdpbusd on 256-bit vectors) where the host has it, else
-// AVX2 (vpmaddubsw + vpmaddwd), else scalar code; the choice is made once at run time.  Q8_0's
-// signed weights go through the usual sign trick (|w| times x with w's sign) so that the
-// unsigned-by-signed byte products never saturate.
+// AVX2 (vpmaddubsw + vpmaddwd), else scalar code; the choice is made once at run time.  The two
+// SIMD paths are one body that differs only in the integer dot (the same sums of 4 byte
+// products per lane), so their rows are identical.  (512-bit vectors, two blocks per vpdpbusd,
+// measured slower on an AVX-512 Xeon: the lane moves that build the two blocks' operands cost
+// more than the halved dot instructions saved.)  Q8_0's signed weights go through the
+// sign trick (|w| times x with w's sign) so that the unsigned-by-signed byte products never
+// saturate.
 #include "cpu_share.hpp"
 
 #include <immintrin.h>
@@ -28,25 +33,27 @@ namespace moe {
 
 namespace {
 
-struct ABlk {   // one 32-value block of a q8_1 row, decoded
-  int8_t q[32];
-  float d;      // the scale as the layer stores it (fp16 -> fp32 exactly for DS4, fp32 for D4)
-  float s;      // DS4: fp16(d * sum q) as fp32 (Q4_1's min term); D4: 0
-};
-
 uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
-// IEEE binary16 from its definition (1 sign, 5 exponent bits biased by 15, 10 fraction bits).
-float half_to_float(uint16_t h) {
-  const int e = (h >> 10) & 31, m = h & 1023;
-  float v;
-  if (e == 0)
-    v = ldexpf((float)m, -24);
-  else if (e == 31)
-    v = m ? NAN : INFINITY;
-  else
-    v = ldexpf((float)(1024 + m), e - 25);
-  return (h & 0x8000) ? -v : v;
+// IEEE binary16 from its definition (1 sign, 5 exponent bits biased by 15, 10 fraction bits),
+// exactly: a normal half's fields move into binary32's (exponent rebiased by 127 - 15); a
+// subnormal is m * 2^-24 (m < 2^10, so the product is exact).  Called for every weight block's
+// scales, so it stays a few integer operations (a libm call per scale dominated small chunks).
+inline float half_to_float(uint16_t h) {
+  const uint32_t e = (h >> 10) & 31u, m = h & 1023u, sign = (uint32_t)(h & 0x8000u) << 16;
+  uint32_t bits;
+  if (e == 0) {
+    const float v = (float)m * 5.9604644775390625e-8f;  // 2^-24
+    memcpy(&bits, &v, 4);
+  } else if (e == 31) {
+    bits = 0x7f800000u | (m << 13);  // infinity, or a NaN keeping its payload
+  } else {
+    bits = ((e + 112u) << 23) | (m << 13);
+  }
+  bits |= sign;
+  float f;
+  memcpy(&f, &bits, 4);
+  return f;
 }
 
 // fp32 -> binary16, round to nearest even, subnormals kept, 65520 and above to infinity.
@@ -67,114 +74,179 @@ uint16_t float_to_half(float f) {
   return (uint16_t)(sign | half);
 }
 
-void quantize_row(const float* v, int n, bool d4, ABlk* out) {
+// A q8_1 row of n values, decoded for the dot products (one contiguous piece of scratch):
+//   q   int8 [n]            the block values, block b at 32 b
+//   dxe float [n/64][16]    per pair of blocks (2i, 2i + 1): dx of block 2i in 8 lanes, then dx of
+//                           block 2i + 1 in 8 lanes (the scale vector the dot products multiply)
+//   sx  float [n/32]        s of each block (DS4: fp16(d * sum q) as fp32; D4: 0)
+struct QRow {
+  const int8_t* q;
+  const float* dxe;
+  const float* sx;
+};
+size_t qrow_bytes(int n) { return (size_t)n + (size_t)(n / 64) * 64 + (size_t)(n / 32) * 4; }
+QRow qrow_at(uint8_t* base, int n) {
+  QRow r;
+  r.q = reinterpret_cast<const int8_t*>(base);
+  r.dxe = reinterpret_cast<const float*>(base + n);
+  r.sx = reinterpret_cast<const float*>(base + n + (size_t)(n / 64) * 64);
+  return r;
+}
+
+// q8_1 of n values v (n a multiple of 128) into a QRow at base.
+void quantize_row(const float* v, int n, bool d4, uint8_t* base) {
+  int8_t* q = reinterpret_cast<int8_t*>(base);
+  float* dxe = reinterpret_cast<float*>(base + n);
+  float* sx = reinterpret_cast<float*>(base + n + (size_t)(n / 64) * 64);
   for (int b = 0; b < n / 32; ++b) {
     const float* x = v + 32 * b;
-    ABlk& o = out[b];
     float amax = 0.0f;
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    float dx = 0.0f, s = 0.0f;
     if (amax == 0.0f) {
-      memset(o.q, 0, 32);
-      o.d = o.s = 0.0f;
-      continue;
-    }
-    const float d = amax / 127.0f;
-    int S = 0;
-    for (int j = 0; j < 32; ++j) {
-      const int q = (int)roundf(x[j] / d);
-      o.q[j] = (int8_t)q;
-      S += q;
-    }
-    if (d4) {
-      o.d = d;
-      o.s = 0.0f;
+      memset(q + 32 * b, 0, 32);
     } else {
-      o.d = half_to_float(float_to_half(d));
-      const float p = d * (float)S;  // rounded to fp32 before the fp16 rounding
-      o.s = half_to_float(float_to_half(p));
+      const float d = amax / 127.0f;
+      int S = 0;
+      for (int j = 0; j < 32; ++j) {
+        const int qj = (int)roundf(x[j] / d);
+        q[32 * b + j] = (int8_t)qj;
+        S += qj;
+      }
+      if (d4) {
+        dx = d;
+      } else {
+        dx = half_to_float(float_to_half(d));
+        const float p = d * (float)S;  // rounded to fp32 before the fp16 rounding
+        s = half_to_float(float_to_half(p));
+      }
     }
+    for (int l = 0; l < 8; ++l) dxe[16 * (b >> 1) + 8 * (b & 1) + l] = dx;
+    sx[b] = s;
   }
 }
 
-constexpr int kChunk = 8;  // activation rows per pass over a weight row
-
-// out[r] = sum over the row's nblk blocks of y_b for activation rows xr[r], r < nr.
+// out[r] = sum over the weight row's nblk blocks of y_b for the activation rows xr[r], r < nr.
 template <int WT>
-void dots_scalar(const uint8_t* wrow, int nblk, const ABlk* const* xr, int nr, float* out) {
+void dots_scalar(const uint8_t* wrow, int nblk, const QRow* xr, int nr, float* out) {
   const int bb = WT == 1 ? 20 : 34;
   for (int r = 0; r < nr; ++r) {
     float acc = 0.0f;
     for (int b = 0; b < nblk; ++b) {
       const uint8_t* blk = wrow + (size_t)b * bb;
-      const ABlk& a = xr[r][b];
+      const int8_t* x = xr[r].q + 32 * b;
+      const float dx = xr[r].dxe[16 * (b >> 1) + 8 * (b & 1)];
       int I = 0;
       if (WT == 1) {
-        for (int j = 0; j < 16; ++j)
-          I += (blk[4 + j] & 15) * a.q[j] + (blk[4 + j] >> 4) * a.q[j + 16];
-        acc += half_to_float(rd16(blk)) * a.d * (float)I + half_to_float(rd16(blk + 2)) * a.s;
+        for (int j = 0; j < 16; ++j) I += (blk[4 + j] & 15) * x[j] + (blk[4 + j] >> 4) * x[j + 16];
+        acc += half_to_float(rd16(blk)) * dx * (float)I + half_to_float(rd16(blk + 2)) * xr[r].sx[b];
       } else {
-        for (int j = 0; j < 32; ++j) I += (int8_t)blk[2 + j] * a.q[j];
-        acc += half_to_float(rd16(blk)) * a.d * (float)I;
+        for (int j = 0; j < 32; ++j) I += (int8_t)blk[2 + j] * x[j];
+        acc += half_to_float(rd16(blk)) * dx * (float)I;
       }
     }
     out[r] = acc;
   }
 }
 
-// The SIMD form of dots_scalar, per activation row 8 lanes of partial dots (4 byte products
-// each); two copies, one per instruction set, so that the AVX2 one never uses AVX-512.
-#define MOE_SIMD_DOTS(NAME, TARGET, DOT8)                                                      \
-  template <int WT>                                                                            \
-  __attribute__((target(TARGET))) void NAME(const uint8_t* wrow, int nblk,                      \
-                                            const ABlk* const* xr, int nr, float* out) {        \
-    const int bb = WT == 1 ? 20 : 34;                                                          \
-    for (int r0 = 0; r0 < nr; r0 += kChunk) {                                                  \
-      const int m = std::min(kChunk, nr - r0);                                                 \
-      __m256 acc[kChunk];                                                                      \
-      float macc[kChunk];                                                                      \
-      for (int i = 0; i < kChunk; ++i) {                                                       \
-        acc[i] = _mm256_setzero_ps();                                                          \
-        macc[i] = 0.0f;                                                                        \
-      }                                                                                        \
-      for (int b = 0; b < nblk; ++b) {                                                         \
-        const uint8_t* blk = wrow + (size_t)b * bb;                                            \
-        __m256i w;                                                                             \
-        if (WT == 1) {                                                                         \
-          const __m128i qs = _mm_loadu_si128(reinterpret_cast<const __m128i*>(blk + 4));       \
-          const __m128i mk = _mm_set1_epi8(15);                                                \
-          w = _mm256_set_m128i(_mm_and_si128(_mm_srli_epi16(qs, 4), mk),                       \
-                               _mm_and_si128(qs, mk));                                         \
-        } else {                                                                               \
-          w = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(blk + 2));                   \
-        }                                                                                      \
-        const __m256i aw = WT == 1 ? w : _mm256_sign_epi8(w, w);                               \
-        const float dw = half_to_float(rd16(blk));                                             \
-        const float mw = WT == 1 ? half_to_float(rd16(blk + 2)) : 0.0f;                        \
-        for (int i = 0; i < m; ++i) {                                                          \
-          const ABlk& a = xr[r0 + i][b];                                                       \
-          __m256i x = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(a.q));               \
-          if (WT != 1) x = _mm256_sign_epi8(x, w);                                             \
-          const __m256i p = DOT8(aw, x);                                                       \
-          acc[i] = _mm256_fmadd_ps(_mm256_cvtepi32_ps(p), _mm256_set1_ps(dw * a.d), acc[i]);   \
-          if (WT == 1) macc[i] += mw * a.s;                                                    \
-        }                                                                                      \
-      }                                                                                        \
-      for (int i = 0; i < m; ++i) {                                                            \
-        const __m128 s4 =                                                                      \
-            _mm_add_ps(_mm256_castps256_ps128(acc[i]), _mm256_extractf128_ps(acc[i], 1));      \
-        const __m128 s2 = _mm_add_ps(s4, _mm_movehl_ps(s4, s4));                               \
-        const __m128 s1 = _mm_add_ss(s2, _mm_shuffle_ps(s2, s2, 1));                           \
-        out[r0 + i] = _mm_cvtss_f32(s1) + macc[i];                                             \
-      }                                                                                        \
-    }                                                                                          \
+// The SIMD paths.  Per pair of blocks and activation row: 16 lanes of 4-product integer dots
+// (lanes 0-7 block 2i, 8-15 block 2i + 1, two 8-lane accumulators), converted to fp32, times
+// dw * dx (exact for DS4: two fp16 significands), added into the accumulators with one fma.  At
+// the end lanes l and l + 8 are added, then the 8 lanes in a fixed tree, then Q4_1's min term,
+// itself an 8-lane dot of the weight row's m with the activation row's s.
+#define MOE_HSUM8(T, v)                                                                  \
+  T __m128 s4_ = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));    \
+  const __m128 s2_ = _mm_add_ps(s4_, _mm_movehl_ps(s4_, s4_));                           \
+  const float hsum_ = _mm_cvtss_f32(_mm_add_ss(s2_, _mm_shuffle_ps(s2_, s2_, 1)));
+
+template <int WT>
+__attribute__((target("avx2,fma"))) inline void unpack_pair_avx2(const uint8_t* blk,
+                                                                 __m256i* w0, __m256i* w1) {
+  const int bb = WT == 1 ? 20 : 34;
+  if (WT == 1) {
+    const __m128i mk = _mm_set1_epi8(15);
+    const __m128i a = _mm_loadu_si128(reinterpret_cast<const __m128i*>(blk + 4));
+    const __m128i b = _mm_loadu_si128(reinterpret_cast<const __m128i*>(blk + bb + 4));
+    *w0 = _mm256_set_m128i(_mm_and_si128(_mm_srli_epi16(a, 4), mk), _mm_and_si128(a, mk));
+    *w1 = _mm256_set_m128i(_mm_and_si128(_mm_srli_epi16(b, 4), mk), _mm_and_si128(b, mk));
+  } else {
+    *w0 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(blk + 2));
+    *w1 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(blk + bb + 2));
+  }
+}
+
+// Q4_1's min term of one activation row: sum_b m_b * s_b as an 8-lane fp32 dot (the same code
+// in both SIMD paths).
+__attribute__((target("avx2,fma"))) inline float mterm8(const float* mw, const float* sx,
+                                                        int nblk) {
+  __m256 a = _mm256_setzero_ps();
+  int b = 0;
+  for (; b + 8 <= nblk; b += 8)
+    a = _mm256_fmadd_ps(_mm256_loadu_ps(mw + b), _mm256_loadu_ps(sx + b), a);
+  if (b < nblk) {  // nblk is a multiple of 4: one half-filled step
+    const __m256 z = _mm256_setzero_ps();
+    a = _mm256_fmadd_ps(_mm256_insertf128_ps(z, _mm_loadu_ps(mw + b), 0),
+                        _mm256_insertf128_ps(z, _mm_loadu_ps(sx + b), 0), a);
+  }
+  MOE_HSUM8(const, a)
+  return hsum_;
+}
+
+// The SIMD paths, one body for both instruction sets (only the integer dot differs).
+#define MOE_SIMD_DOTS(NAME, TARGET, DOT8)                                                       \
+  template <int WT>                                                                             \
+  __attribute__((target(TARGET))) void NAME(const uint8_t* wrow, int nblk, const QRow* xr,      \
+                                            int nr, float* out, float* mw) {                   \
+    constexpr int kChunk = 4; /* rows per pass over the weight row (16 accumulators) */         \
+    const int bb = WT == 1 ? 20 : 34;                                                           \
+    if (WT == 1)                                                                                \
+      for (int b = 0; b < nblk; ++b) mw[b] = half_to_float(rd16(wrow + (size_t)b * bb + 2));   \
+    for (int r0 = 0; r0 < nr; r0 += kChunk) {                                                   \
+      const int m = std::min(kChunk, nr - r0);                                                  \
+      __m256 lo[kChunk], hi[kChunk];                                                            \
+      for (int i = 0; i < kChunk; ++i) lo[i] = hi[i] = _mm256_setzero_ps();                     \
+      for (int b = 0; b < nblk; b += 2) {                                                       \
+        const uint8_t* blk = wrow + (size_t)b * bb;                                             \
+        __m256i w0, w1;                                                                         \
+        unpack_pair_avx2<WT>(blk, &w0, &w1);                                                    \
+        const __m256i a0 = WT == 1 ? w0 : _mm256_sign_epi8(w0, w0);                             \
+        const __m256i a1 = WT == 1 ? w1 : _mm256_sign_epi8(w1, w1);                             \
+        const __m256 d0 = _mm256_set1_ps(half_to_float(rd16(blk)));                             \
+        const __m256 d1 = _mm256_set1_ps(half_to_float(rd16(blk + bb)));                        \
+        for (int i = 0; i < m; ++i) {                                                           \
+          const QRow& x = xr[r0 + i];                                                           \
+          __m256i x0 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(x.q + 32 * b));      \
+          __m256i x1 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(x.q + 32 * b + 32)); \
+          if (WT != 1) {                                                                        \
+            x0 = _mm256_sign_epi8(x0, w0);                                                      \
+            x1 = _mm256_sign_epi8(x1, w1);                                                      \
+          }                                                                                     \
+          const float* e = x.dxe + 8 * b; /* the pair's 16 lanes */                             \
+          lo[i] = _mm256_fmadd_ps(_mm256_cvtepi32_ps(DOT8(a0, x0)),                              \
+                                  _mm256_mul_ps(d0, _mm256_loadu_ps(e)), lo[i]);                \
+          hi[i] = _mm256_fmadd_ps(_mm256_cvtepi32_ps(DOT8(a1, x1)),                              \
+                                  _mm256_mul_ps(d1, _mm256_loadu_ps(e + 8)), hi[i]);            \
+        }                                                                                       \
+      }                                                                                         \
+      for (int i = 0; i < m; ++i) {                                                             \
+        const __m256 v = _mm256_add_ps(lo[i], hi[i]);                                           \
+        MOE_HSUM8(const, v)                                                                     \
+        out[r0 + i] = WT == 1 ? hsum_ + mterm8(mw, xr[r0 + i].sx, nblk) : hsum_;                \
+      }                                                                                         \
+    }                                                                                           \
   }
 
-#define MOE_DOT8_AVX2(aw, x) _mm256_madd_epi16(_mm256_maddubs_epi16(aw, x), _mm256_set1_epi16(1))
-#define MOE_DOT8_VNNI(aw, x) _mm256_dpbusd_epi32(_mm256_setzero_si256(), aw, x)
+#define MOE_DOT8_AVX2(a, x) _mm256_madd_epi16(_mm256_maddubs_epi16(a, x), _mm256_set1_epi16(1))
+#define MOE_DOT8_VNNI(a, x) _mm256_dpbusd_epi32(_mm256_setzero_si256(), a, x)
 MOE_SIMD_DOTS(dots_avx2, "avx2,fma", MOE_DOT8_AVX2)
 MOE_SIMD_DOTS(dots_vnni, "avx2,fma,avx512f,avx512vl,avx512bw,avx512vnni", MOE_DOT8_VNNI)
 
-typedef void (*DotsFn)(const uint8_t*, int, const ABlk* const*, int, float*);
+typedef void (*DotsFn)(const uint8_t*, int, const QRow*, int, float*, float*);
+
+template <int WT>
+void dots_scalar_fn(const uint8_t* w, int nblk, const QRow* xr, int nr, float* out, float*) {
+  dots_scalar<WT>(w, nblk, xr, nr, out);
+}
 
 int detect_isa_host();
 
@@ -189,8 +261,8 @@ int detect_isa() {
 
 int detect_isa_host() {
   if (__builtin_cpu_supports("avx512vnni") && __builtin_cpu_supports("avx512vl") &&
-      __builtin_cpu_supports("avx512bw") && __builtin_cpu_supports("avx2") &&
-      __builtin_cpu_supports("fma"))
+      __builtin_cpu_supports("avx512bw") && __builtin_cpu_supports("avx512f") &&
+      __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma"))
     return 2;
   if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) return 1;
   return 0;
@@ -203,8 +275,8 @@ int isa() {
 
 DotsFn dots_for(int wt) {
   const int i = isa();
-  if (wt == 1) return i == 2 ? dots_vnni<1> : i == 1 ? dots_avx2<1> : dots_scalar<1>;
-  return i == 2 ? dots_vnni<0> : i == 1 ? dots_avx2<0> : dots_scalar<0>;
+  if (wt == 1) return i == 2 ? dots_vnni<1> : i == 1 ? dots_avx2<1> : dots_scalar_fn<1>;
+  return i == 2 ? dots_vnni<0> : i == 1 ? dots_avx2<0> : dots_scalar_fn<0>;
 }
 
 }  // namespace
@@ -222,37 +294,38 @@ void cpu_expert_rows(int wtype, int H, int F, const uint8_t* expert, const float
   const int bb = wt == 1 ? 20 : 34;
   const int nbh = H / 32, nbf = F / 32;
   const DotsFn dots = dots_for(wt);
-  sc.act.resize((size_t)n_rows * nbh * sizeof(ABlk));
-  sc.hq.resize((size_t)n_rows * nbf * sizeof(ABlk));
+  const size_t xrb = qrow_bytes(H), hrb = qrow_bytes(F);
+  sc.act.resize((size_t)n_rows * xrb);
+  sc.hq.resize((size_t)n_rows * hrb);
   sc.g.resize((size_t)n_rows * F);
   sc.u.resize((size_t)n_rows * F);
-  sc.h.resize((size_t)n_rows * F);
-  ABlk* act = reinterpret_cast<ABlk*>(sc.act.data());
-  ABlk* hq = reinterpret_cast<ABlk*>(sc.hq.data());
-  std::vector<const ABlk*> xr(n_rows), hr(n_rows);
+  sc.h.resize((size_t)n_rows * F + (size_t)std::max(nbh, nbf));  // the tail holds m (Q4_1)
+  float* mw = sc.h.data() + (size_t)n_rows * F;
+  std::vector<QRow> xr(n_rows), hr(n_rows);
   std::vector<float> tmp(n_rows);
   for (int r = 0; r < n_rows; ++r) {
-    quantize_row(x_rows[r], H, d4, act + (size_t)r * nbh);
-    xr[r] = act + (size_t)r * nbh;
-    hr[r] = hq + (size_t)r * nbf;
+    quantize_row(x_rows[r], H, d4, sc.act.data() + (size_t)r * xrb);
+    xr[r] = qrow_at(sc.act.data() + (size_t)r * xrb, H);
+    hr[r] = qrow_at(sc.hq.data() + (size_t)r * hrb, F);
   }
   const size_t mat = (size_t)F * nbh * bb;  // bytes of gate (and of up)
   const uint8_t* gate = expert;
   const uint8_t* up = expert + mat;
   const uint8_t* down = expert + 2 * mat;
   for (int n = 0; n < F; ++n) {
-    dots(gate + (size_t)n * nbh * bb, nbh, xr.data(), n_rows, tmp.data());
+    dots(gate + (size_t)n * nbh * bb, nbh, xr.data(), n_rows, tmp.data(), mw);
     for (int r = 0; r < n_rows; ++r) sc.g[(size_t)r * F + n] = tmp[r];
-    dots(up + (size_t)n * nbh * bb, nbh, xr.data(), n_rows, tmp.data());
+    dots(up + (size_t)n * nbh * bb, nbh, xr.data(), n_rows, tmp.data(), mw);
     for (int r = 0; r < n_rows; ++r) sc.u[(size_t)r * F + n] = tmp[r];
   }
   for (size_t k = 0; k < (size_t)n_rows * F; ++k) {
     const float g = sc.g[k];
     sc.h[k] = g / (1.0f + expf(-g)) * sc.u[k];
   }
-  for (int r = 0; r < n_rows; ++r) quantize_row(sc.h.data() + (size_t)r * F, F, d4, hq + (size_t)r * nbf);
+  for (int r = 0; r < n_rows; ++r)
+    quantize_row(sc.h.data() + (size_t)r * F, F, d4, sc.hq.data() + (size_t)r * hrb);
   for (int i = 0; i < H; ++i) {
-    dots(down + (size_t)i * nbf * bb, nbf, hr.data(), n_rows, tmp.data());
+    dots(down + (size_t)i * nbf * bb, nbf, hr.data(), n_rows, tmp.data(), mw);
     for (int r = 0; r < n_rows; ++r) out[(size_t)r * H + i] = tmp[r];
   }
 }
