@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 #define MOE_MAX_GROUP 16     /* experts per group buffer ([G1] "What": MMQ_GROUP = 16) */
 #define MOE_MAX_E 2048       /* largest expert count the kernels accept */
 #define MOE_MAX_K 64         /* largest routes per token */
@@ -72,7 +72,10 @@ typedef enum {
     MOE_EUNSUPPORTED = -2,  /* a valid request the library does not implement (H or F not a
                                multiple of 128, E > MOE_MAX_E, K > MOE_MAX_K, unknown type) */
     MOE_EWORKSPACE = -3,    /* the workspace is smaller than the matching *_workspace_size() */
-    MOE_EHIP = -4           /* a HIP launch or runtime call failed */
+    MOE_EHIP = -4,          /* a HIP launch or runtime call failed */
+    MOE_ENOMEM = -5         /* host memory or host threads could not be obtained (the streamed walk,
+                               its CPU share, the host planner and the stage profiler allocate on
+                               the host); the call stopped and its outputs are unspecified */
 } moe_status;
 
 /* Weight type, and with it the q8_1 layout of the activations the MMQ reads: Q8_0 and Q4_1 take
@@ -302,8 +305,8 @@ int moe_walk_destroy(moe_walk *walk);
  * walk's copy stream.  The arena must stay unchanged until `stream` has passed this call.
  * Calls on one walk must not overlap; the walk's slot map and events carry over between calls,
  * so a slot read by one call is refilled by the next only after that read. */
-/* After a MOE_EHIP from this call the walk's slot map may name events that were never recorded:
- * destroy the walk. */
+/* After a MOE_EHIP or MOE_ENOMEM from this call the walk's slot map may name events that were
+ * never recorded: destroy the walk. */
 int moe_prefill_layer_streamed(moe_walk *walk, const float *x, int T, int H, int F, int E, int K,
                                const int32_t *topk_idx, const float *topk_w, int wtype,
                                const void *host_arena, size_t arena_bytes,
@@ -343,7 +346,8 @@ int moe_walk_stats(const moe_walk *walk, int64_t *stats, int n);
  *   max_T, H: the largest T and the H of the calls (a call outside them returns MOE_EINVAL);
  *   max_rows: at most this many rows per call go to the host (its staging capacity).
  * Allocates pinned host buffers (max_T x H and max_rows x H fp32), device buffers (max_rows x H
- * fp32) and starts the threads; MOE_EHIP if they cannot be made (the previous setting stays).
+ * fp32) and starts the threads; MOE_EHIP if the HIP buffers or events cannot be made, MOE_ENOMEM
+ * if the host threads or their scratch cannot (either way the previous setting stays).
  * Not a fallback: the HIP path never hands work to the host unless the caller asks for it here. */
 int moe_walk_cpu_share(moe_walk *walk, double share, int max_tokens, int threads, int max_T,
                        int H, int max_rows);

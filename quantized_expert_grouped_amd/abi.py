@@ -32,7 +32,7 @@ WALK_STATS = ("copies", "bytes", "batches", "waits", "copy_waits", "skip_flushes
 OP_COPY, OP_GATHER, OP_MMQ = 1, 2, 3
 
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EWORKSPACE",
-          -4: "MOE_EHIP"}
+          -4: "MOE_EHIP", -5: "MOE_ENOMEM"}
 
 # name -> (restype, argtypes); the order of this table is the header's order
 P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t

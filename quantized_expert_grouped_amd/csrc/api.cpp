@@ -40,6 +40,7 @@ const char* moe_strerror(int status) {
     case MOE_EUNSUPPORTED: return "unsupported shape or type";
     case MOE_EWORKSPACE: return "workspace too small";
     case MOE_EHIP: return "HIP launch or runtime error";
+    case MOE_ENOMEM: return "host memory or threads could not be obtained";
     default: return "unknown status";
   }
 }
@@ -334,7 +335,11 @@ int moe_profile_begin(int n_calls) {
   if (n_calls < 1 || n_calls > 100000) return MOE_EINVAL;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   destroy_events();
-  g_prof_ev.resize((size_t)n_calls * kEvPerCall);
+  try {
+    g_prof_ev.assign((size_t)n_calls * kEvPerCall, nullptr);
+  } catch (...) {
+    return MOE_ENOMEM;
+  }
   for (hipEvent_t& e : g_prof_ev) {
     if (hipEventCreate(&e) != hipSuccess) {
       e = nullptr;

@@ -332,7 +332,17 @@ void cpu_expert_rows(int wtype, int H, int F, const uint8_t* expert, const float
 
 // ---- the pool -------------------------------------------------------------------------------
 CpuPool::CpuPool(int n_threads) {
-  for (int i = 1; i < n_threads; ++i) workers_.emplace_back([this, i] { loop(i); });
+  try {
+    for (int i = 1; i < n_threads; ++i) workers_.emplace_back([this, i] { loop(i); });
+  } catch (...) {  // a thread could not start: stop and join the ones that did, then report
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+    }
+    go_.notify_all();
+    for (std::thread& t : workers_) t.join();
+    throw;
+  }
 }
 
 CpuPool::~CpuPool() {

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <memory>
 #include <new>
@@ -257,7 +258,7 @@ int moe_walk_cpu_share(moe_walk* walk, double share, int max_tokens, int threads
       (long long)max_T * MOE_MAX_K > (1LL << 30) || (long long)max_rows * H > (1LL << 40))
     return MOE_EINVAL;
   std::unique_ptr<HostShare> hs(new (std::nothrow) HostShare);
-  if (!hs) return MOE_EHIP;
+  if (!hs) return MOE_ENOMEM;
   hs->share = share < 0 ? -1.0 : share;
   hs->cur = share < 0 ? 0.25 : share;
   hs->max_tokens = max_tokens;
@@ -280,14 +281,16 @@ int moe_walk_cpu_share(moe_walk* walk, double share, int max_tokens, int threads
             hipMalloc(reinterpret_cast<void**>(&hs->d_dst), (size_t)max_rows * 4) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&hs->d_skip), kMaxE) == hipSuccess &&
             hipEventCreate(&hs->t0) == hipSuccess && hipEventCreate(&hs->t1) == hipSuccess;
-  if (ok) {
-    hs->pool.reset(new (std::nothrow) CpuPool(threads));
-    ok = hs->pool != nullptr;
-    hs->scratch.resize(threads);
-  }
   if (!ok) {
     free_host_share(hs.get());
     return MOE_EHIP;
+  }
+  try {  // threads and their scratch (no exception crosses the C boundary)
+    hs->pool.reset(new CpuPool(threads));
+    hs->scratch.resize(threads);
+  } catch (...) {
+    free_host_share(hs.get());
+    return MOE_ENOMEM;
   }
   free_host_share(walk->share.get());
   walk->share = std::move(hs);
@@ -305,21 +308,24 @@ int moe_walk_plan(const int32_t* counts, const int32_t* order, int n_active, int
                   int32_t* used_of, int32_t* cursor, int32_t* next_event, int32_t* ops,
                   int max_ops) {
   if (!ops || max_ops < 0) return MOE_EINVAL;
-  std::vector<Op> v;
-  const int n = plan(counts, order, n_active, E, ring_start, streamed, group_size, n_slots, flags,
-                     used_of, cursor, next_event, v);
-  if (n < 0) return n;
-  if (n > max_ops) return MOE_EWORKSPACE;
-  std::copy(v.begin(), v.end(), reinterpret_cast<Op*>(ops));
-  return n;
+  try {
+    std::vector<Op> v;
+    const int n = plan(counts, order, n_active, E, ring_start, streamed, group_size, n_slots,
+                       flags, used_of, cursor, next_event, v);
+    if (n < 0) return n;
+    if (n > max_ops) return MOE_EWORKSPACE;
+    std::copy(v.begin(), v.end(), reinterpret_cast<Op*>(ops));
+    return n;
+  } catch (...) {  // host memory: no exception crosses the C boundary
+    return MOE_ENOMEM;
+  }
 }
 
-int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, int E, int K,
-                               const int32_t* topk_idx, const float* topk_w, int wtype,
-                               const void* host_arena, size_t arena_bytes,
-                               const int64_t* host_off, const void* const* resident,
-                               int group_size, int ring_start, int flags, void* ws,
-                               size_t ws_bytes, float* out, void* stream) {
+static int layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, int E, int K,
+                          const int32_t* topk_idx, const float* topk_w, int wtype,
+                          const void* host_arena, size_t arena_bytes, const int64_t* host_off,
+                          const void* const* resident, int group_size, int ring_start, int flags,
+                          void* ws, size_t ws_bytes, float* out, void* stream) {
   if (!walk || !host_off || !resident) return MOE_EINVAL;
   if ((flags & ~(MOE_WALK_GATHER_ONE | MOE_WALK_NO_SKIP_FLUSH)) != 0) return MOE_EINVAL;
   Layout L;
@@ -446,6 +452,7 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
     }
   } join;
   std::vector<int> stage_first(n_host + 1, 0);  // the expert's first staged row
+  std::atomic<bool> host_failed{false};
   std::chrono::steady_clock::time_point host_t0;
   if (hs) {
     for (int e = 0; e < E; ++e) hs->h_skip[e] = w.streamed[e] == kHost ? 1 : 0;
@@ -457,16 +464,20 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
     if (n_host > 0) {
       host_t0 = std::chrono::steady_clock::now();
       hs->pool->start(n_host, [&, hs](int j, int worker) {
-        const int e = host_experts[j];
-        const int cnt = h_counts[e], first = stage_first[j];
-        std::vector<const float*> xr(cnt);
-        for (int i = 0; i < cnt; ++i) {
-          const int32_t r = (int32_t)(off[e] + i);
-          xr[i] = hs->h_x + (size_t)(hs->h_src[r] / K) * H;
-          hs->h_dst[first + i] = r;
+        try {  // a worker's exception would end the process: flag it instead
+          const int e = host_experts[j];
+          const int cnt = h_counts[e], first = stage_first[j];
+          std::vector<const float*> xr(cnt);
+          for (int i = 0; i < cnt; ++i) {
+            const int32_t r = (int32_t)(off[e] + i);
+            xr[i] = hs->h_x + (size_t)(hs->h_src[r] / K) * H;
+            hs->h_dst[first + i] = r;
+          }
+          cpu_expert_rows(wtype, H, F, arena + host_off[e], xr.data(), cnt,
+                          hs->h_rows + (size_t)first * H, hs->scratch[worker]);
+        } catch (...) {
+          host_failed.store(true);
         }
-        cpu_expert_rows(wtype, H, F, arena + host_off[e], xr.data(), cnt,
-                        hs->h_rows + (size_t)first * H, hs->scratch[worker]);
       });
       join.pool = hs->pool.get();
     }
@@ -539,6 +550,7 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
     if (n_host > 0) {
       join.pool = nullptr;
       hs->pool->wait();
+      if (host_failed.load()) return MOE_ENOMEM;
       const double ns = std::chrono::duration<double, std::nano>(
                             std::chrono::steady_clock::now() - host_t0).count();
       hs->host_ns = ns / n_host;
@@ -563,15 +575,34 @@ int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int
   return MOE_OK;
 }
 
+int moe_prefill_layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, int E, int K,
+                               const int32_t* topk_idx, const float* topk_w, int wtype,
+                               const void* host_arena, size_t arena_bytes,
+                               const int64_t* host_off, const void* const* resident,
+                               int group_size, int ring_start, int flags, void* ws,
+                               size_t ws_bytes, float* out, void* stream) {
+  try {  // the walk's host vectors: no exception crosses the C boundary
+    return layer_streamed(walk, x, T, H, F, E, K, topk_idx, topk_w, wtype, host_arena,
+                          arena_bytes, host_off, resident, group_size, ring_start, flags, ws,
+                          ws_bytes, out, stream);
+  } catch (...) {
+    return MOE_ENOMEM;
+  }
+}
+
 int moe_cpu_expert_rows(int wtype, int H, int F, const void* expert, const float* x, int n_rows,
                         float* out) {
   if (!expert || !x || !out || n_rows < 1) return MOE_EINVAL;
   if (!valid_wtype(wtype)) return MOE_EUNSUPPORTED;
   if (H < 128 || H % 128 != 0 || F < 128 || F % 128 != 0) return MOE_EUNSUPPORTED;
-  std::vector<const float*> xr(n_rows);
-  for (int r = 0; r < n_rows; ++r) xr[r] = x + (size_t)r * H;
-  CpuScratch sc;
-  cpu_expert_rows(wtype, H, F, static_cast<const uint8_t*>(expert), xr.data(), n_rows, out, sc);
+  try {
+    std::vector<const float*> xr(n_rows);
+    for (int r = 0; r < n_rows; ++r) xr[r] = x + (size_t)r * H;
+    CpuScratch sc;
+    cpu_expert_rows(wtype, H, F, static_cast<const uint8_t*>(expert), xr.data(), n_rows, out, sc);
+  } catch (...) {
+    return MOE_ENOMEM;
+  }
   return MOE_OK;
 }
 

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert abi.abi_version() == 6
+    assert abi.abi_version() == 7
     assert abi.block_bytes(abi.Q8_0) == 34 and abi.block_bytes(abi.Q4_1) == 20
     assert abi.block_bytes(7) == 0
     assert abi.block_bytes(abi.Q8_0_D4) == 34
@@ -50,6 +50,8 @@ def test_version_and_sizes():
     assert abi.expert_bytes(2048, 512, abi.Q4_1) == 1966080
     assert abi.q8_1_row_bytes(2048) == 2304
     assert abi.strerror(-3) == "workspace too small"
+    assert abi.strerror(-5) == "host memory or threads could not be obtained"
+    assert abi.STATUS[-5] == "MOE_ENOMEM"
     ws = abi.workspace_size(8192, 2048, 512, 512, 10, abi.Q4_1, 16)
     R = 8192 * 10
     # at least q8 rows of x and h, Dm, and one group position per expert
