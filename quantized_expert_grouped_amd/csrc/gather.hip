@@ -62,16 +62,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_group_kernel(GatherPtrs
   copy_span(p.src[j], dst + (size_t)(first_pos + j) * pos_stride, bytes, blockIdx.x, gridDim.x);
 }
 
-__global__ __launch_bounds__(kGatherThreads) void gather_all_kernel(
-    const uint8_t* __restrict__ pool, const int64_t* __restrict__ expert_off,
-    const int32_t* __restrict__ order, const int32_t* __restrict__ n_active, size_t bytes,
-    uint8_t* __restrict__ dst, size_t stride) {
-  const int pos = blockIdx.z * gridDim.y + blockIdx.y;  // group * group_size + position in group
-  if (pos >= *n_active) return;
-  copy_span(pool + expert_off[order[pos]], dst + (size_t)pos * stride, bytes, blockIdx.x,
-            gridDim.x);
-}
-
 // ---- the MMQ layout -------------------------------------------------------------------------
 // The grouped matmul stages its weights as tiles of 64 rows by 128 values (4 blocks), so the
 // group buffer holds every matrix as those tile-stages, each one contiguous: for tile j, stage
@@ -250,17 +240,19 @@ __global__ __launch_bounds__(kGatherThreads) void gather_mmq_all_kernel(
     const int32_t* __restrict__ order, const int32_t* __restrict__ n_active, int H, int F,
     uint8_t* __restrict__ dst, size_t stride) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[Pack<WT>::kLds];
-  // Workgroups reach the 8 XCDs round-robin; renumber them so that each XCD moves a contiguous
-  // run of (expert, item) pairs, keeping the neighbouring slices of a tile, which share cache
-  // lines at their edges, in one L2.  (blockIdx.z = group and blockIdx.y = position in it, as
-  // in one group's launch.)
+  // Workgroups reach the 8 XCDs round-robin; renumber the live ones so that each XCD moves a
+  // contiguous run of (expert, item) pairs, keeping the neighbouring slices of a tile, which share
+  // cache lines at their edges, in one L2.  The runs split the routed positions' items, not the
+  // grid (sized for every expert): split over the grid, the XCDs whose runs fell past the routed
+  // positions had nothing to move (skewed routing left half the chip idle).  (blockIdx.z = group
+  // and blockIdx.y = position in it, as in one group's launch.)
   const int items = gridDim.x;
-  const int n = items * gridDim.y * gridDim.z;
+  const int live = *n_active * items;
   const int id = blockIdx.x + items * (blockIdx.y + gridDim.y * blockIdx.z);
+  if (id >= live) return;
   const int xcd = id % 8;
-  const int work = xcd * (n / 8) + min(xcd, n % 8) + id / 8;
+  const int work = xcd * (live / 8) + min(xcd, live % 8) + id / 8;
   const int pos = work / items;
-  if (pos >= *n_active) return;
   pack_item<WT>(pool + expert_off[order[pos]], dst + (size_t)pos * stride, H, F, work % items,
                 lds);
 }
@@ -280,17 +272,6 @@ hipError_t launch_gather_group(const GatherPtrs& p, int n, size_t bytes, uint8_t
                                int first_pos, size_t pos_stride, hipStream_t s) {
   const dim3 grid(parts_for(bytes), n);
   gather_group_kernel<<<grid, kGatherThreads, 0, s>>>(p, bytes, dst, first_pos, pos_stride);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather_all(const uint8_t* pool, const int64_t* expert_off, const int32_t* order,
-                             const int32_t* n_active, int max_slots, int group_size, size_t bytes,
-                             uint8_t* dst, size_t stride, hipStream_t s) {
-  // blockIdx.z = group, blockIdx.y = expert within the group, as in one group's launch
-  const int groups = (max_slots + group_size - 1) / group_size;
-  const dim3 grid(parts_for(bytes), group_size, groups);
-  gather_all_kernel<<<grid, kGatherThreads, 0, s>>>(pool, expert_off, order, n_active, bytes,
-                                                    dst, stride);
   return hipGetLastError();
 }
 

@@ -69,17 +69,13 @@ struct GatherPtrs {
 };
 hipError_t launch_gather_group(const GatherPtrs& p, int n, size_t bytes, uint8_t* dst,
                                int first_pos, size_t pos_stride, hipStream_t s);
-// Every group of the layer in one launch: active expert i (ring order) -> dst + i*stride.
-hipError_t launch_gather_all(const uint8_t* pool, const int64_t* expert_off,
-                             const int32_t* order, const int32_t* n_active, int max_slots,
-                             int group_size, size_t bytes, uint8_t* dst, size_t stride,
-                             hipStream_t s);
-
-// The same positions, each expert written in the MMQ layout the grouped matmul reads (64-row
-// tiles of 4-block stages, headers first; the raw expert's size).
+// The same copy, each expert written in the MMQ layout the grouped matmul reads (64-row tiles of
+// 4-block stages, headers first; the raw expert's size).
 hipError_t launch_gather_group_mmq(const GatherPtrs& p, int n, int wtype, int H, int F,
                                    uint8_t* dst, int first_pos, size_t pos_stride,
                                    hipStream_t s);
+// Every group of the layer in one launch: active expert i (ring order) -> dst + i*stride, in
+// the MMQ layout.
 hipError_t launch_gather_all_mmq(const uint8_t* pool, const int64_t* expert_off,
                                  const int32_t* order, const int32_t* n_active, int max_slots,
                                  int group_size, int wtype, int H, int F, uint8_t* dst,
