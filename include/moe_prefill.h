@@ -185,7 +185,8 @@ int moe_gather_group_mmq(const void *const *src_ptrs, int n, int wtype, int H, i
  *   MOE_EPI_SWIGLU_Q8_1:   q8_1 rows of h = silu(g)*u (n_out values); debug_h, if not NULL, gets the
  *                          fp32 h [* x n_out] that was quantised
  *   MOE_EPI_I32_BLOCKDOTS: int32 [* x n_out x k_in/32], the raw I_b
- * n_out and k_in: multiples of 128.  group_buf, pos_stride and mat_offset: multiples of 16 bytes;
+ * n_out and k_in: multiples of 128, the matrix (both matrices for MOE_EPI_SWIGLU_Q8_1) below
+ * 4 GiB, else MOE_EUNSUPPORTED.  group_buf, pos_stride and mat_offset: multiples of 16 bytes;
  * act_q8: 16-byte aligned.  The matrix must lie inside each position's bytes (caller's duty). */
 int moe_mmq_grouped(int wtype, const void *group_buf, size_t pos_stride, size_t mat_offset,
                     int n_out, int k_in, const int32_t *group_experts, int n_group,
@@ -207,7 +208,8 @@ int moe_combine(const float *Dm, const int32_t *slot, const float *topk_w, int T
  * group_size (1..16) and ring_start (0..E-1) set which experts share a group buffer; the output is
  * bit-identical for every choice ([G1] "What": every byte reaches the position one copy per expert
  * gives it; [G2] "What changes": neither the products nor their order change).  ws: moe_workspace_size(...) bytes.
- * out fp32 [T x H].  H, F multiples of 128; E <= 2048; K <= min(E, 64). */
+ * out fp32 [T x H].  H, F multiples of 128 (gate and up together, and down, each below 4 GiB);
+ * E <= 2048; K <= min(E, 64). */
 int moe_prefill_layer(const float *x, int T, int H, int F, int E, int K,
                       const int32_t *topk_idx, const float *topk_w, int wtype,
                       const void *pool, const int64_t *expert_off, size_t expert_bytes,

@@ -185,6 +185,8 @@ int moe_mmq_grouped(int wtype, const void* group_buf, size_t pos_stride, size_t 
   if (epilogue < MOE_EPI_F32 || epilogue > MOE_EPI_I32_BLOCKDOTS) return MOE_EINVAL;
   if (!valid_wtype(wtype)) return MOE_EUNSUPPORTED;
   if (n_out < 128 || n_out % 128 != 0 || k_in < 128 || k_in % 128 != 0) return MOE_EUNSUPPORTED;
+  if (!mmq_offsets_fit(n_out, k_in, wtype, epilogue == MOE_EPI_SWIGLU_Q8_1))
+    return MOE_EUNSUPPORTED;
   if (!aligned(group_buf, 16) || pos_stride % 16 != 0 || mat_offset % 16 != 0 ||
       !aligned(act_q8, 16) || !aligned(out, 4) || !aligned(debug_h, 4))
     return MOE_EINVAL;

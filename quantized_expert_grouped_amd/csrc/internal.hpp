@@ -112,6 +112,12 @@ struct MmqProblem {
   int n_group;
 };
 hipError_t launch_mmq(const MmqProblem& p, hipStream_t s);
+// The MMQ addresses a weight matrix's bytes by 32-bit offsets from the matrix's start (the gate
+// and up matrices from the gate's): they must stay below 4 GiB.
+inline bool mmq_offsets_fit(long long n_out, long long k_in, int wtype, bool gate_and_up) {
+  const long long bb = wtype == 1 ? 20 : 34;
+  return (gate_and_up ? 2 : 1) * n_out * (k_in / 32) * bb < (1LL << 32);
+}
 // The layer's MMQ launch is one-dimensional: n-tiles x m-tiles workgroups must fit in x.
 constexpr long long kMaxGridX = 0x7fffffffLL;
 inline long long mmq_layer_workgroups(int n_out_gu, int n_out_dn, int max_tiles) {

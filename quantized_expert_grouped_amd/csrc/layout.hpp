@@ -85,6 +85,8 @@ inline int check_layer_args(const float* x, int T, int H, int F, int E, int K,
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256)) return MOE_EINVAL;
   if (!make_layout(T, H, F, E, K, wtype, L)) return MOE_EINVAL;
   if (mmq_layer_workgroups(F, H, L->max_tiles) > kMaxGridX) return MOE_EUNSUPPORTED;
+  if (!mmq_offsets_fit(F, H, wtype, true) || !mmq_offsets_fit(H, F, wtype, false))
+    return MOE_EUNSUPPORTED;
   if (ws_bytes < L->total) return MOE_EWORKSPACE;
   return MOE_OK;
 }

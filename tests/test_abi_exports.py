@@ -156,3 +156,31 @@ def test_packed_layer_host_validation():
     assert call(pool=264) == -1                  # pool not 16-byte aligned
     assert call(rs=8) == -1                      # ring_start >= E
     assert call(ws_bytes=16) == -3               # workspace too small
+
+
+def test_host_checks_refuse_matrices_beyond_32_bit_offsets():
+    """The MMQ addresses a weight matrix by 32-bit offsets: larger matrices are refused on the host
+    (MOE_EUNSUPPORTED) before anything is enqueued, so no pointer here is ever dereferenced."""
+    L = abi.lib()
+    fake = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never touched
+    experts = (ctypes.c_int32 * 1)(0)
+    # gate and up of 32,768 x 2,048 Q8_0 blocks: 4.56 GB > 4 GiB
+    rc = L.moe_mmq_grouped(0, fake, 1 << 33, 0, 32768, 65536, ctypes.cast(experts, ctypes.c_void_p),
+                           1, fake, 1, fake, 1, fake, None, None)
+    assert rc == -2
+    # the same shape as a single matrix (fp32 epilogue): 2.28 GB, accepted by this check, then
+    # refused further on only by what the fake pointers cannot satisfy
+    rc = L.moe_mmq_grouped(0, fake, 1 << 33, 0, 32768, 65536, ctypes.cast(experts, ctypes.c_void_p),
+                           1, fake, 1, fake, 0, ctypes.c_void_p(3), None, None)
+    assert rc == -1                          # out not 4-byte aligned: MOE_EINVAL
+    # the layer: H = 65,536, F = 32,768 (gate + up 4.56 GB)
+    eb = abi.expert_bytes(65536, 32768, 0)
+    rc = L.moe_prefill_layer(fake, 8, 65536, 32768, 16, 2, fake, fake, 0, fake, fake, eb, 16, 0,
+                             fake, 1 << 62, fake, None)
+    assert rc == -2
+    # control: H = F = 32,768 (gate + up 2.28 GB, down 1.14 GB) passes that check and stops at the
+    # workspace size (MOE_EWORKSPACE)
+    eb = abi.expert_bytes(32768, 32768, 0)
+    rc = L.moe_prefill_layer(fake, 8, 32768, 32768, 16, 2, fake, fake, 0, fake, fake, eb, 16, 0,
+                             fake, 0, fake, None)
+    assert rc == -3
