@@ -14,6 +14,7 @@ CPU baseline times the plain C oracle on a bounded sample of the same workload.
 
 Other lines (not the headline; each prints its own JSON line):
     --walk streamed [--ring-slots N] [--resident-frac f] [--gather-one] [--walk-group-size G]
+                    [--mmq-per-group]
         routing + moe_prefill_layer_streamed: experts copied from a pinned host arena through a
         ring of device slots; reports the host->device rate against PCIe 5.0 x16.
     --walk packed       routing + moe_prefill_layer_packed (experts kept in the MMQ layout).
@@ -214,7 +215,8 @@ def streamed_walk(args, c, layer, x, logits, out, dev):
     keep = set(np.random.default_rng(7).permutation(c.E)[:n_res].tolist())
     base = layer.pool.data_ptr()
     resident = [base + int(c.expert_off[e]) if e in keep else 0 for e in range(c.E)]
-    flags = abi.WALK_GATHER_ONE if args.gather_one else 0
+    flags = (abi.WALK_GATHER_ONE if args.gather_one else 0) | \
+        (abi.WALK_MMQ_PER_GROUP if args.mmq_per_group else 0)
     G = args.walk_group_size
     share = None
     if args.cpu_share is not None:
@@ -260,6 +262,7 @@ def streamed_walk(args, c, layer, x, logits, out, dev):
                    "T": c.T, "walk": "streamed",
                    "ring_slots": args.ring_slots, "resident_experts": n_res,
                    "group_size": G, "gather_one": bool(args.gather_one),
+                   "mmq_per_group": bool(args.mmq_per_group),
                    "cpu_share": args.cpu_share,
                    **({"cpu_share_max_tokens": args.cpu_share_max_tokens,
                        "cpu_share_isa": abi.cpu_share_isa(),
@@ -458,6 +461,8 @@ def main():
     ap.add_argument("--resident-frac", type=float, default=0.0,
                     help="streamed walk: the fraction of experts held in HBM (not copied)")
     ap.add_argument("--walk-group-size", type=int, default=16)
+    ap.add_argument("--mmq-per-group", action="store_true",
+                    help="streamed walk: one MMQ launch pair per group (never merged)")
     ap.add_argument("--gather-one", action="store_true",
                     help="streamed walk: one gather launch, wait and event per expert")
     ap.add_argument("--cpu-share", default=None,

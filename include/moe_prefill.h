@@ -271,13 +271,17 @@ size_t moe_workspace_offset(int which, int T, int H, int F, int E, int K, int wt
  * skipped while the group is open ([G2] "What changes": the entries waiting in an open batch
  * never exceed one group), or when the next copy needs a ring slot that the open batch itself holds (a ring
  * smaller than a group).  After a group's last batch its MMQ gate/up and down launch on that
- * group's m-tiles, so a group's products overlap later groups' copies.  The output is
+ * group's m-tiles, so a group's products overlap later groups' copies; the MMQs of consecutive
+ * groups whose later batches need no copy wait (resident experts, copies already covered) go out
+ * as one launch pair over their m-tiles, which fills the GPU where per-group launches would not
+ * (MOE_WALK_MMQ_PER_GROUP keeps one pair per group).  The output is
  * bit-identical to moe_prefill_layer's for the same arguments: every expert's bytes reach the
  * position the layer gives them, and the matmuls are the same launches' arithmetic. */
 #define MOE_WALK_EVENTS 64
 #define MOE_WALK_GATHER_ONE 1      /* one expert per batch: one wait, launch and event per expert
                                       ([G2] "What changes", the opt-out) */
 #define MOE_WALK_NO_SKIP_FLUSH 2   /* a skipped ring entry does not launch the open batch */
+#define MOE_WALK_MMQ_PER_GROUP 4   /* one MMQ launch pair per group, never merged (the pages' form) */
 
 typedef struct moe_walk moe_walk;
 

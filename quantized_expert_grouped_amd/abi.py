@@ -24,7 +24,7 @@ N_STAGES = 6
 STAGES = ("maps", "quantize", "gather", "gate_up", "down", "combine")
 
 WALK_EVENTS = 64
-WALK_GATHER_ONE, WALK_NO_SKIP_FLUSH = 1, 2
+WALK_GATHER_ONE, WALK_NO_SKIP_FLUSH, WALK_MMQ_PER_GROUP = 1, 2, 4
 WALK_NSTATS = 16
 WALK_STATS = ("copies", "bytes", "batches", "waits", "copy_waits", "skip_flushes", "slot_flushes",
               "mmq_launches", "routing_syncs", "transfers", "host_experts", "host_rows",

@@ -59,7 +59,7 @@ int plan(const int32_t* counts, const int32_t* order, int n_active, int E, int r
   if (E < 1 || E > kMaxE || ring_start < 0 || ring_start >= E || n_active < 0 || n_active > E ||
       G < 1 || G > MOE_MAX_GROUP || n_slots < 1 || *cursor < 0 || *cursor >= n_slots ||
       *next_event < 0 || *next_event >= kEvents ||
-      (flags & ~(MOE_WALK_GATHER_ONE | MOE_WALK_NO_SKIP_FLUSH)) != 0)
+      (flags & ~(MOE_WALK_GATHER_ONE | MOE_WALK_NO_SKIP_FLUSH | MOE_WALK_MMQ_PER_GROUP)) != 0)
     return MOE_EINVAL;
   // order must be the routed entries in ring order
   int j = 0;
@@ -327,7 +327,8 @@ static int layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, i
                           const void* const* resident, int group_size, int ring_start, int flags,
                           void* ws, size_t ws_bytes, float* out, void* stream) {
   if (!walk || !host_off || !resident) return MOE_EINVAL;
-  if ((flags & ~(MOE_WALK_GATHER_ONE | MOE_WALK_NO_SKIP_FLUSH)) != 0) return MOE_EINVAL;
+  if ((flags & ~(MOE_WALK_GATHER_ONE | MOE_WALK_NO_SKIP_FLUSH | MOE_WALK_MMQ_PER_GROUP)) != 0)
+    return MOE_EINVAL;
   Layout L;
   const size_t eb = moe_expert_bytes(H, F, wtype);
   const int rc = check_layer_args(x, T, H, F, E, K, topk_idx, topk_w, wtype, eb, group_size,
@@ -482,6 +483,24 @@ static int layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, i
       join.pool = hs->pool.get();
     }
   }
+  // The MMQs of consecutive groups are deferred and launched together until a batch must wait
+  // for copies (a deferred launch then goes first, so it still overlaps those copies): a
+  // batch that needs no wait runs at once on the compute stream, so launching the earlier
+  // group's MMQ after it delays nothing.  The slots a batch reads are released by its own
+  // event, and the MMQs read only group positions, so the order is free.
+  const bool per_group = (flags & MOE_WALK_MMQ_PER_GROUP) != 0;
+  int mmq_p0 = -1, mmq_p1 = -1;  // the deferred MMQs' positions [p0, p1)
+  auto flush_mmq = [&]() -> bool {
+    if (mmq_p0 < 0) return true;
+    const int t0 = w.tile_first[mmq_p0], t1 = w.tile_first[mmq_p1];
+    mmq_p0 = mmq_p1 = -1;
+    if (t1 <= t0) return true;  // cannot happen: a routed expert has at least one m-tile
+    gu.tiles = dn.tiles = mo.tiles + t0;
+    gu.tile_count = dn.tile_count = t1 - t0;
+    if (!ok(launch_mmq(gu, s)) || !ok(launch_mmq(dn, s))) return false;
+    w.stats[kStMmq] += 2;
+    return true;
+  };
   const size_t nops = w.ops.size();
   for (size_t k = 0; k < nops; ++k) {
     const int32_t* v = w.ops[k].v;
@@ -516,7 +535,8 @@ static int layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, i
       k = r;
     } else if (v[0] == kOpGather) {
       if (v[3]) {
-        if (!ok(hipEventRecord(w.copied, w.copy)) || !ok(hipStreamWaitEvent(s, w.copied, 0)))
+        if (!flush_mmq() || !ok(hipEventRecord(w.copied, w.copy)) ||
+            !ok(hipStreamWaitEvent(s, w.copied, 0)))
           return MOE_EHIP;
         ++w.stats[kStWaits];
       }
@@ -535,14 +555,17 @@ static int layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, i
       if (v[5] == kWhySkip) ++w.stats[kStSkipFlush];
       if (v[5] == kWhySlot) ++w.stats[kStSlotFlush];
     } else {
-      const int t0 = w.tile_first[v[2]], t1 = w.tile_first[v[2] + v[3]];
-      if (t1 <= t0) continue;  // cannot happen: a routed expert has at least one m-tile
-      gu.tiles = dn.tiles = mo.tiles + t0;
-      gu.tile_count = dn.tile_count = t1 - t0;
-      if (!ok(launch_mmq(gu, s)) || !ok(launch_mmq(dn, s))) return MOE_EHIP;
-      w.stats[kStMmq] += 2;
+      if (mmq_p0 >= 0 && mmq_p1 == v[2]) {
+        mmq_p1 = v[2] + v[3];  // the next group: one launch over both
+      } else {
+        if (!flush_mmq()) return MOE_EHIP;
+        mmq_p0 = v[2];
+        mmq_p1 = v[2] + v[3];
+      }
+      if (per_group && !flush_mmq()) return MOE_EHIP;
     }
   }
+  if (!flush_mmq()) return MOE_EHIP;
   if (hs) {
     if (!ok(hipEventRecord(hs->t1, s))) return MOE_EHIP;
     hs->timed_experts = n_streamed - n_host;

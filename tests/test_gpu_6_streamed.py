@@ -72,6 +72,7 @@ WALKS = [
     (16, 16, abi.WALK_GATHER_ONE, "none"),
     (3, 7, abi.WALK_NO_SKIP_FLUSH, "third"),
     (2, 16, 0, "all"),
+    (96, 16, abi.WALK_MMQ_PER_GROUP, "half"),
 ]
 
 
@@ -108,7 +109,13 @@ def test_streamed_walk_equals_resident_layer(orc, case):
         assert st["copies"] == int(np.sum(~mask[routed]))
         assert st["bytes"] == st["copies"] * c.expert_bytes
         assert st["waits"] <= st["batches"] and st["routing_syncs"] == 1
-        assert st["mmq_launches"] == 2 * ((n + G - 1) // G)
+        groups = (n + G - 1) // G
+        if flags & abi.WALK_MMQ_PER_GROUP:
+            assert st["mmq_launches"] == 2 * groups
+        else:  # consecutive groups' MMQs merge unless a batch between them waits for copies
+            assert 2 <= st["mmq_launches"] <= 2 * groups
+            if res == "all":
+                assert st["mmq_launches"] == 2
         if flags & abi.WALK_GATHER_ONE:
             assert st["batches"] == n
         s.walk.close()
@@ -194,7 +201,7 @@ def test_streamed_host_validation():
     small = c.expert_off.max() + c.expert_bytes - 1          # the last expert does not fit
     assert abi.raw_prefill_layer_streamed(**args(arena_bytes=int(small))) == -1
     assert abi.raw_prefill_layer_streamed(**args(host_arena=None)) == -1
-    assert abi.raw_prefill_layer_streamed(**args(flags=4)) == -1
+    assert abi.raw_prefill_layer_streamed(**args(flags=8)) == -1       # an unknown flag bit
     assert abi.raw_prefill_layer_streamed(**args(group_size=17)) == -1
     assert s.walk.stats()["routing_syncs"] == 0              # nothing was enqueued
     s.walk.close()
