@@ -29,7 +29,8 @@
 //   otherwise: weight rows n0+64wc.. and n0+64wc+32...
 // K loop: stages of 4 blocks (128 values, one q8_1 group).  Stages stream into a ring of two LDS
 // buffers with direct global->LDS loads (global_load_lds_dwordx4), one stage ahead of the
-// MFMAs, at three workgroups per CU, so the registers hold no staged data and no VALU moves it.
+// MFMAs, at three or four workgroups per CU, so the registers hold no staged data and no VALU
+// moves it.
 // The weights come from the group buffer's MMQ layout (64-row tiles of one stage, each
 // contiguous, every row's block headers first), so a workgroup's weight stage is two contiguous
 // runs, and in LDS the rows sit 80 (Q4_1) or 136 (Q8_0) bytes apart.  q8_1 rows keep their
