@@ -13,9 +13,11 @@
 //   acc = fma(float(I_b), S_b, acc)         the only per-element VALU work (convert + fma)
 //   Q4_1 adds sum_b mw_b * sx_b             a true sum over blocks: an f16 MFMA whose C input
 //                                           is the accumulator itself
-// Both halves of the wavefront feed the same scale into the f16 MFMAs (no zero lanes), so they
-// produce exactly 2*S_b and 2*sum(mw*sx); the accumulator carries that factor 2 and is halved
-// once at the end, which in binary floating point changes no rounding.  Blocks are taken in
+// The f16 MFMAs' K-sum runs over both lane halves.  In the fp32-output kernel the second half's
+// activation-scale operand is zero, so each product dx_b * dw_b (and mw_b * sx_b) enters once;
+// the SwiGLU kernel feeds the scale from both halves, so it gets exactly 2*S_b and 2*mw_b*sx_b,
+// and halves its accumulators once before the epilogue, which in binary floating point changes
+// no rounding (one multiply per tile instead of masks held in registers).  Blocks are taken in
 // ascending order and every output element is accumulated by one lane in one fixed instruction
 // sequence, so results do not depend on the tiling, the group size, the ring start or the row's
 // place in its tile.
@@ -276,6 +278,14 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   const v16i izero = {0};
   const v16f fzero = {0.0f};
 
+  // The scale operand's selectors: the fp16 kept in the low half of a dword, or moved to the high
+  // half (v_perm selector byte 0x0c is a zero byte); in the fp32-output kernel, lane half 1
+  // contributes zeros.
+  constexpr bool kOnce = EPI == 0;
+  const bool zero_half = kOnce && half != 0;
+  const uint32_t keep_lo = zero_half ? 0u : 0xffffu, keep_hi = keep_lo << 16;
+  const uint32_t to_hi = zero_half ? 0x0c0c0c0cu : 0x01000c0cu;
+
   // stage t of the sweep's n-tile j (EPI 0: n-tile j's weights start 2j 64-row tiles later)
   auto issue = [&](StageBuf<WT>& buf, int j, int t) {
     issue_stage<WT>(buf, plan, abase + (size_t)t * kARow,
@@ -328,21 +338,24 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
         f0 = b_raw<WT>(brow0, b + 1, half);
         f1 = b_raw<WT>(brow1, b + 1, half);
       }
-      // 2 * dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero).  D4's fp32
+      // dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero).  D4's fp32
       // dx_b goes in as two fp16 (hi = fp16(dx), lo = fp16(dx - hi)) in slots 2b, 2b+1, both
       // facing dw_b: the MFMA adds hi*dw + lo*dw, each product exact in fp32
-      // f16 operand of dx_b: fp16 slot 2b (Q4_1, D4) or b (Q8_0), every other slot zero
+      // f16 operand of dx_b: fp16 slot 2b (Q4_1, D4) or b (Q8_0), every other slot zero, and
+      // every slot zero in lane half 1
       v4i za = {0, 0, 0, 0};
       if (WT == 1) {
-        za[b] = (int)((uint32_t)hx[b] & 0xffffu);
+        za[b] = (int)((uint32_t)hx[b] & keep_lo);
       } else if (WT == kWtQ8_0D4) {
         const float dx = __int_as_float(hx[b]);
         const _Float16 hi = (_Float16)dx;
         const _Float16 lo = (_Float16)(dx - (float)hi);
-        za[b] = (int)((uint32_t)__builtin_bit_cast(uint16_t, hi) |
-                         ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
+        za[b] = (int)(((uint32_t)__builtin_bit_cast(uint16_t, hi) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16)) &
+                      (keep_lo | keep_hi));
       } else {
-        za[b >> 1] = (b & 1) ? (int)((uint32_t)hx[b] << 16) : (int)((uint32_t)hx[b] & 0xffffu);
+        za[b >> 1] = (b & 1) ? (int)__builtin_amdgcn_perm(0u, (uint32_t)hx[b], to_hi)
+                             : (int)((uint32_t)hx[b] & keep_lo);
       }
       const v8h sx = __builtin_bit_cast(v8h, za);
       if (WT == 1 && EPI == 1) {  // one column tile after the other (fits 128 VGPRs)
@@ -380,32 +393,36 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
         acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
     }
     if (WT == 1) {
-      // 2 * sum over the stage's blocks of sx_b * mw_b: (0, s_b) against (d_b, m_b)
+      // sum over the stage's blocks of sx_b * mw_b: (0, s_b) against (d_b, m_b), zeros in lane
+      // half 1
       v4i hs;
 #pragma unroll
-      for (int b = 0; b < kKB; ++b) hs[b] = (int)((uint32_t)hx[b] & 0xffff0000u);
+      for (int b = 0; b < kKB; ++b) hs[b] = (int)((uint32_t)hx[b] & keep_hi);
       const v8h sxs = __builtin_bit_cast(v8h, hs);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxs, hw0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxs, hw1, acc1, 0, 0, 0);
     }
   };
 
-  // EPI 0: n-tile j's fp32 rows (the doubled scales' factor 2 removed, exactly), then the
-  // accumulators cleared for the next n-tile.  A uniform base and one 32-bit lane offset
-  // (64 rows x n_out floats stay below 2^31 bytes), computed at the store rather than hoisted
-  // out of the stage loop, where they would hold registers.
+  // EPI 0: n-tile j's fp32 rows, then the accumulators cleared for the next n-tile.  Register i
+  // holds row 32 wr + 8 (i / 4) + 4 half + i % 4: its address is a wavefront-uniform row base
+  // (scalar arithmetic) plus one 32-bit lane offset that does not change with i (4 half rows
+  // and the lane's column; below 2^31 bytes as 64 rows x n_out floats are); column tile ct1
+  // lies 32 floats after ct0.
   auto store_f32 = [&](int j) {
-    float* ob = reinterpret_cast<float*>(p.out) + (size_t)row0 * p.n_out + n0 + j * kRowsN;
-    uint32_t off = (uint32_t)((32 * wr + 4 * half) * p.n_out + l32);
-    asm volatile("" : "+v"(off));
+    const int wu = wave_id();  // wr and ct0 as scalars
+    const char* ob =
+        reinterpret_cast<const char*>(p.out) +
+        ((size_t)(row0 + 32 * (wu >> 1)) * p.n_out + n0 + j * kRowsN + 64 * (wu & 1)) * 4;
+    const uint32_t off = (uint32_t)((4 * half * p.n_out + l32) * 4);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = 32 * wr + 8 * (i >> 2) + 4 * half + (i & 3);
       if (row < nrows) {
-        ob[off + 32 * ct0] = 0.5f * acc0[i];
-        ob[off + 32 * ct1] = 0.5f * acc1[i];
+        float* dst = (float*)(ob + (size_t)(8 * (i >> 2) + (i & 3)) * p.n_out * 4 + off);
+        dst[0] = acc0[i];
+        dst[32] = acc1[i];
       }
-      off += (uint32_t)p.n_out * ((i & 3) == 3 ? 5u : 1u);
       acc0[i] = 0.0f;
       acc1[i] = 0.0f;
     }
