@@ -214,6 +214,42 @@ def test_layer_step_in_a_hip_graph(orc):
                                            c.E)) <= TOL
 
 
+def test_layer_calls_on_two_streams_overlap(orc):
+    """Two layers (own pools and workspaces, different shapes and weight types) stepped on two
+    streams at once, three rounds with no synchronisation inside a round: every result equals
+    that layer's eager step on the default stream bit for bit (the library keeps no state a
+    call could share with another)."""
+    ca = synth.make_case("streamA", T=900, H=512, F=256, E=32, K=4, wtype=synth.Q4_1, seed=31)
+    cb = synth.make_case("streamB", T=700, H=384, F=384, E=20, K=3, wtype=synth.Q8_0, seed=32,
+                         zipf=1.1)
+    la, lb = _layer(ca), _layer(cb)
+    xa, ga, xb, gb = dev(ca.x), dev(ca.logits), dev(cb.x), dev(cb.logits)
+    note("two layers eager, then overlapped on two streams")
+    want_a, want_b = host(la.step(xa, ga)), host(lb.step(xb, gb))
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for r in range(3):
+        oa = torch.empty((ca.T, ca.H), dtype=torch.float32, device="cuda")
+        ob = torch.empty((cb.T, cb.H), dtype=torch.float32, device="cuda")
+        sa.wait_stream(torch.cuda.current_stream())
+        sb.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(sa):
+            la.step(xa, ga, oa)
+        with torch.cuda.stream(sb):
+            lb.step(xb, gb, ob)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for r, (oa, ob) in enumerate(outs):
+        assert np.array_equal(host(oa), want_a), r
+        assert np.array_equal(host(ob), want_b), r
+    ia, wa = orc.route_topk(ca.logits, ca.K)
+    assert rel_err(want_a, orc.prefill_layer(ca.x, ia, wa, ca.wtype, ca.pool, ca.expert_off,
+                                             ca.F, ca.E)) <= TOL
+    ib, wb = orc.route_topk(cb.logits, cb.K)
+    assert rel_err(want_b, orc.prefill_layer(cb.x, ib, wb, cb.wtype, cb.pool, cb.expert_off,
+                                             cb.F, cb.E)) <= TOL
+
+
 def test_layer_out_of_range_ids_contribute_nothing(orc):
     """Routes naming no real expert (ids -1, E, E + 7): the layer counts them in its workspace's
     status word, every other token's row equals the oracle's for the original routing, and a
