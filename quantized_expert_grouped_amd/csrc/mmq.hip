@@ -9,10 +9,12 @@
 //                                           (K = 32 is exactly one block)
 //   S_b = dx_b * dw_b                       exact in fp32 (two fp16 significands); for a whole
 //                                           32x32 tile an outer product: one
-//                                           v_mfma_f32_32x32x16_f16
+//                                           v_mfma_f32_32x32x8_f16 (on gfx950 it issues faster
+//                                           than the 32x32x16 form, and one K-slot is all an
+//                                           outer product needs)
 //   acc = fma(float(I_b), S_b, acc)         the only per-element VALU work (convert + fma)
 //   Q4_1 adds sum_b mw_b * sx_b             a true sum over blocks: an f16 MFMA whose C input
-//                                           is the accumulator itself
+//                                           is the accumulator itself, once per stage
 // The f16 MFMAs' K-sum runs over both lane halves.  In the fp32-output kernel the second half's
 // activation-scale operand is zero, so each product dx_b * dw_b (and mw_b * sx_b) enters once;
 // the SwiGLU kernel feeds the scale from both halves, so it gets exactly 2*S_b and 2*mw_b*sx_b,
@@ -55,7 +57,8 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
@@ -231,9 +234,10 @@ __device__ __forceinline__ v4i b_unpack(const v4i& r) {
   return (v4i){(int)(x0 & m), (int)(x1 & m), (int)((x0 >> 4) & m), (int)((x1 >> 4) & m)};
 }
 
-// The f16 MFMA operand of a row's weight headers: Q4_1 (d_b, m_b) in fp16 slots 2b, 2b+1;
-// Q8_0 d_b in slot b (slots 4..7 zero); Q8_0 read with D4 activations: d_b in slots 2b and 2b+1
-// (they meet the two fp16 halves of the activation's fp32 d).
+// A row's weight headers as four dwords of fp16 pairs, the scale MFMAs' weight operands taken a
+// dword pair at a time: Q4_1 (d_b, m_b) in dword b; Q8_0 d_0..d_3 in dwords 0 and 1 (2 and 3
+// unused); Q8_0 read with D4 activations (d_b, d_b) in dword b (they meet the two fp16 halves of
+// the activation's fp32 d).
 template <int WT>
 __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
   if (WT == 1) return *reinterpret_cast<const v4i*>(brow);
@@ -285,6 +289,7 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   const bool zero_half = kOnce && half != 0;
   const uint32_t keep_lo = zero_half ? 0u : 0xffffu, keep_hi = keep_lo << 16;
   const uint32_t to_hi = zero_half ? 0x0c0c0c0cu : 0x01000c0cu;
+  const uint32_t sel_s = zero_half ? 0x0c0c0c0cu : 0x07060302u;
 
   // stage t of the sweep's n-tile j (EPI 0: n-tile j's weights start 2j 64-row tiles later)
   auto issue = [&](StageBuf<WT>& buf, int j, int t) {
@@ -321,8 +326,25 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
     }
     // activation headers (d_b, s_b) of the row, weight headers of the two column tiles
     const v4i hx = *reinterpret_cast<const v4i*>(arow);
-    const v8h hw0 = __builtin_bit_cast(v8h, b_header<WT>(brow0));
-    const v8h hw1 = __builtin_bit_cast(v8h, b_header<WT>(brow1));
+    const v4i hw0 = b_header<WT>(brow0);
+    const v4i hw1 = b_header<WT>(brow1);
+    if (WT == 1) {
+      // sum over the stage's blocks of sx_b * mw_b (added first: its operands die before the
+      // block loop): (s_0, s_1, s_2, s_3) against
+      // (m_0, m_1, m_2, m_3), both gathered from the headers' high halves; zeros in lane half 1
+      // of the fp32-output kernel
+      const v4h ss = __builtin_bit_cast(
+          v4h, (v2i){(int)__builtin_amdgcn_perm((uint32_t)hx[1], (uint32_t)hx[0], sel_s),
+                     (int)__builtin_amdgcn_perm((uint32_t)hx[3], (uint32_t)hx[2], sel_s)});
+      const v4h m0 = __builtin_bit_cast(
+          v4h, (v2i){(int)__builtin_amdgcn_perm((uint32_t)hw0[1], (uint32_t)hw0[0], 0x07060302u),
+                     (int)__builtin_amdgcn_perm((uint32_t)hw0[3], (uint32_t)hw0[2], 0x07060302u)});
+      const v4h m1 = __builtin_bit_cast(
+          v4h, (v2i){(int)__builtin_amdgcn_perm((uint32_t)hw1[1], (uint32_t)hw1[0], 0x07060302u),
+                     (int)__builtin_amdgcn_perm((uint32_t)hw1[3], (uint32_t)hw1[2], 0x07060302u)});
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(ss, m0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(ss, m1, acc1, 0, 0, 0);
+    }
     // Q4_1: the LDS reads of each block's operands are issued one block ahead of its MFMAs
     v4i fa = a_frag<WT>(arow, 0, half), f0 = b_raw<WT>(brow0, 0, half),
         f1 = b_raw<WT>(brow1, 0, half);
@@ -338,31 +360,37 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
         f0 = b_raw<WT>(brow0, b + 1, half);
         f1 = b_raw<WT>(brow1, b + 1, half);
       }
-      // dx_b * dw_b: dx_b alone in its slot meets dw_b (a Q4_1 m_b faces a zero).  D4's fp32
-      // dx_b goes in as two fp16 (hi = fp16(dx), lo = fp16(dx - hi)) in slots 2b, 2b+1, both
-      // facing dw_b: the MFMA adds hi*dw + lo*dw, each product exact in fp32
-      // f16 operand of dx_b: fp16 slot 2b (Q4_1, D4) or b (Q8_0), every other slot zero, and
-      // every slot zero in lane half 1
-      v4i za = {0, 0, 0, 0};
-      if (WT == 1) {
-        za[b] = (int)((uint32_t)hx[b] & keep_lo);
-      } else if (WT == kWtQ8_0D4) {
+      // S_b = dx_b * dw_b from v_mfma_f32_32x32x8_f16: a lane half supplies four fp16 K-slots
+      // (two dwords); the weight operand is one dword pair of the header, the activation operand
+      // holds dx_b in the slot facing dw_b and zeros elsewhere.  Q4_1 and D4: header dword b
+      // holds block b's two weight fp16, the pair (2 (b / 2), 2 (b / 2) + 1); Q8_0: d_0..d_3 in
+      // slots 0..3 of the pair (0, 1).  D4's fp32 dx_b goes in as two fp16 (hi = fp16(dx),
+      // lo = fp16(dx - hi)) in both slots of its dword, both facing dw_b: the MFMA adds
+      // hi*dw + lo*dw, each product exact in fp32.  Lane half 1 holds zeros in the fp32-output
+      // kernel and the same values in the SwiGLU kernel.
+      uint32_t sv;
+      if (WT == kWtQ8_0D4) {
         const float dx = __int_as_float(hx[b]);
         const _Float16 hi = (_Float16)dx;
         const _Float16 lo = (_Float16)(dx - (float)hi);
-        za[b] = (int)(((uint32_t)__builtin_bit_cast(uint16_t, hi) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16)) &
-                      (keep_lo | keep_hi));
+        sv = ((uint32_t)__builtin_bit_cast(uint16_t, hi) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16)) &
+             (keep_lo | keep_hi);
+      } else if (WT == 1 || (b & 1) == 0) {
+        sv = (uint32_t)hx[b] & keep_lo;
       } else {
-        za[b >> 1] = (b & 1) ? (int)__builtin_amdgcn_perm(0u, (uint32_t)hx[b], to_hi)
-                             : (int)((uint32_t)hx[b] & keep_lo);
+        sv = __builtin_amdgcn_perm(0u, (uint32_t)hx[b], to_hi);
       }
-      const v8h sx = __builtin_bit_cast(v8h, za);
+      const int dsel = WT == 0 ? (b >> 1) : (b & 1);   // the dword of the pair dx_b goes in
+      const v4h sx = __builtin_bit_cast(v4h, dsel ? (v2i){0, (int)sv} : (v2i){(int)sv, 0});
+      const int pair = WT == 0 ? 0 : (b >> 1);
+      const v4h w0 = __builtin_bit_cast(v4h, pair ? (v2i){hw0[2], hw0[3]} : (v2i){hw0[0], hw0[1]});
+      const v4h w1 = __builtin_bit_cast(v4h, pair ? (v2i){hw1[2], hw1[3]} : (v2i){hw1[0], hw1[1]});
       if (WT == 1 && EPI == 1) {  // one column tile after the other (fits 128 VGPRs)
         {
           const v16i I0 =
               __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x0), izero, 0, 0, 0);
-          const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
+          const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x8f16(sx, w0, fzero, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4 * NG; ++i) acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
         }
@@ -370,16 +398,16 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
         {
           const v16i I1 =
               __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x1), izero, 0, 0, 0);
-          const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw1, fzero, 0, 0, 0);
+          const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x8f16(sx, w1, fzero, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4 * NG; ++i) acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
         }
         continue;
       }
       const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x0), izero, 0, 0, 0);
-      const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
+      const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x8f16(sx, w0, fzero, 0, 0, 0);
       const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b_unpack<WT>(x1), izero, 0, 0, 0);
-      const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw1, fzero, 0, 0, 0);
+      const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x8f16(sx, w1, fzero, 0, 0, 0);
       // each tile's int and scale MFMAs back to back, so tile 0's convert + fma wait on two
       // MFMAs rather than four; in the fp32-output kernel a scheduling barrier also keeps the
       // compiler from moving them (measured: t32k down -4%, t2k -2.7%; the SwiGLU kernel is
@@ -391,16 +419,6 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
 #pragma unroll
       for (int i = 0; i < 4 * NG; ++i)
         acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
-    }
-    if (WT == 1) {
-      // sum over the stage's blocks of sx_b * mw_b: (0, s_b) against (d_b, m_b), zeros in lane
-      // half 1
-      v4i hs;
-#pragma unroll
-      for (int b = 0; b < kKB; ++b) hs[b] = (int)((uint32_t)hx[b] & keep_hi);
-      const v8h sxs = __builtin_bit_cast(v8h, hs);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxs, hw0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sxs, hw1, acc1, 0, 0, 0);
     }
   };
 
