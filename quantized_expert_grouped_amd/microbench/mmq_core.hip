@@ -2,13 +2,15 @@
 // the loop, no barriers), so that what it times is the instruction mix alone.
 //
 // Part 1, MFMA throughput: every wavefront runs independent accumulator chains of one MFMA shape;
-// the result is the time per MFMA per SIMD and the chip-wide rate it implies.
+// the result is the time per MFMA per SIMD and the chip-wide rate it implies.  Besides the shapes
+// the kernels' int8 products use, the f16 shapes that can form a 32x32 outer product of scales:
+// 32x32x16, 32x32x8, and the two-block 32x32x4 (two 32x32 outputs at once).
 //
 // Part 2, the MMQ's per-block work for one wavefront's two 32x32 output tiles (what the grouped
-// matmul issues per 32-value block): two v_mfma_i32_32x32x32_i8 (the block dots I), two
-// v_mfma_f32_32x32x16_f16 (the scale products S), and per output element a convert of I to fp32
-// and one fma into the accumulator.  Mixes (the time is per such "wave-block", per SIMD):
-//   full             the kernel's mix
+// matmul issues per 32-value block): two v_mfma_i32_32x32x32_i8 (the block dots I), the scale
+// products S for both tiles, and per output element a convert of I to fp32 and one fma into the
+// accumulator.  Mixes (the time is per such "wave-block", per SIMD):
+//   full             two v_mfma_f32_32x32x16_f16 for the scale products (the kernel's first form)
 //   no convert       fma on I's bits (wrong values, timing only)
 //   no f16 MFMA      S held in registers
 //   no i8 MFMA       I held in registers
@@ -26,7 +28,19 @@
 //                    16-byte reads per tile, one address per half-wavefront), dx is one fp16 per
 //                    lane.  The orientation this needs: lanes = activation rows, registers =
 //                    weight rows.
+//   deep pipe        all four MFMAs of block b+1 issued before block b's 64 VALU ops, whose
+//                    operands were produced a whole block earlier (two register sets; spills
+//                    above two wavefronts per SIMD)
+//   mul regs         S on the VALU by one v_mul_f32 per element from fp32 registers (no LDS)
+//   mul lds          the same with the 16 activation scales per block read from an fp32 table
+//                    in LDS (four 16-byte broadcast reads)
+//   2b scales        both tiles' S from one two-block v_mfma_f32_32x32x4_f16
+//   x8 scales        each tile's S from one v_mfma_f32_32x32x8_f16 (the kernel's mix)
 // each at 2, 3 and 4 wavefronts per SIMD (set by the LDS a workgroup reserves).
+// Part 3 checks the lane layouts the kernel relies on for the two legacy f16 shapes (D register
+// i of lane l holds row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32; the 32x32x8 K-sum runs over
+// both lane halves, four K-slots each; the two-block form takes block k's operands from lanes
+// 32k..32k+31).
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 
@@ -35,6 +49,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef int v2i_ __attribute__((ext_vector_type(2)));
 
 #define CHECK(x)                                                                        \
   do {                                                                                  \
@@ -46,7 +61,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
   } while (0)
 
 // ---- part 1 ------------------------------------------------------------------------------------
-enum { R_I8_32 = 0, R_F16_32 = 1, R_I8_16 = 2, R_F16_16 = 3 };
+enum { R_I8_32 = 0, R_F16_32 = 1, R_I8_16 = 2, R_F16_16 = 3, R_F16_2B = 4, R_F16_X8 = 5, R_F32_2B = 6 };
 
 template <int S>
 __global__ __launch_bounds__(256, 2) void rate_kernel(const int* __restrict__ in,
@@ -55,7 +70,30 @@ __global__ __launch_bounds__(256, 2) void rate_kernel(const int* __restrict__ in
   const v4i a = {in[lane], in[lane + 64], in[lane + 128], in[lane + 192]};
   const v4i b = {in[lane + 256], in[lane + 320], in[lane + 384], in[lane + 448]};
   float t = 0.f;
-  if (S == R_I8_32 || S == R_F16_32) {
+  if (S == R_F16_2B || S == R_F16_X8 || S == R_F32_2B) {
+    typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+    typedef float v32f __attribute__((ext_vector_type(32)));
+    const v4h ah = __builtin_bit_cast(v4h, (v2i_){a[0], a[1]});
+    const v4h bh = __builtin_bit_cast(v4h, (v2i_){b[0], b[1]});
+    if (S == R_F16_X8) {
+      v16f cf[4];
+      for (int j = 0; j < 4; ++j) cf[j] = (v16f){0.f};
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cf[j] = __builtin_amdgcn_mfma_f32_32x32x8f16(ah, bh, cf[j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) for (int i = 0; i < 16; ++i) t += cf[j][i];
+    } else {
+      v32f cf[4];
+      for (int j = 0; j < 4; ++j) for (int i = 0; i < 32; ++i) cf[j][i] = 0.f;
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (S == R_F16_2B) cf[j] = __builtin_amdgcn_mfma_f32_32x32x4f16(ah, bh, cf[j], 0, 0, 0);
+          else cf[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(__int_as_float(a[0]), __int_as_float(b[0]), cf[j], 0, 0, 0);
+        }
+      for (int j = 0; j < 4; ++j) for (int i = 0; i < 32; ++i) t += cf[j][i];
+    }
+  } else if (S == R_I8_32 || S == R_F16_32) {
     v16i ci[4];
     v16f cf[4];
     for (int j = 0; j < 4; ++j) {
@@ -119,10 +157,10 @@ double rate(int ncu, const int* din, float* dout, double macs, int per_iter, dou
 }
 
 // ---- part 2 ------------------------------------------------------------------------------------
-enum { M_FULL, M_NOCVT, M_NOF16, M_NOI8, M_MFMA, M_VALU, M_BIAS, M_PIPE, M_AGPR, M_VS, M_COUNT };
+enum { M_FULL, M_NOCVT, M_NOF16, M_NOI8, M_MFMA, M_VALU, M_BIAS, M_PIPE, M_AGPR, M_VS, M_DEEP, M_MULR, M_MULL, M_2B, M_X8, M_COUNT };
 static const char* kMixName[M_COUNT] = {"full", "no convert", "no f16 MFMA", "no i8 MFMA",
                                         "MFMAs only", "VALU only", "bias + add", "pipelined",
-                                        "i8 into AGPRs", "VALU scales"};
+                                        "i8 into AGPRs", "VALU scales", "deep pipe", "mul regs", "mul lds", "2b scales", "x8 scales"};
 
 template <int M, int W>
 __global__ __launch_bounds__(256, W) void mix_kernel(const int* __restrict__ in,
@@ -196,6 +234,106 @@ __global__ __launch_bounds__(256, W) void mix_kernel(const int* __restrict__ in,
       for (int i = 0; i < 16; ++i) {
         const float S1 = __builtin_fmaf((float)dx, (float)(i & 1 ? d1[i >> 1].y : d1[i >> 1].x), 0.0f);
         acc1[i] = fmaf((float)I1[i], S1, acc1[i]);
+      }
+    }
+  } else if (M == M_DEEP) {
+    // block b+1's four MFMAs issued before block b's VALU work (whose MFMAs finished a block ago)
+    v16i Ia0, Ia1, Ib0, Ib1;
+    v16f Sa0, Sa1, Sb0, Sb1;
+    auto issue = [&](int blk, v16i& I0, v16i& I1, v16f& S0, v16f& S1) {
+      next_operands(blk);
+      const v8h sx = __builtin_bit_cast(v8h, sa);
+      I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sx, hw0, fzero, 0, 0, 0);
+      I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(hw0, sx, fzero, 0, 0, 0);
+    };
+    auto valu = [&](const v16i& I0, const v16i& I1, const v16f& S0, const v16f& S1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
+        acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
+      }
+    };
+    issue(0, Ia0, Ia1, Sa0, Sa1);
+    for (int blk = 1; blk < nblocks; blk += 2) {
+      issue(blk, Ib0, Ib1, Sb0, Sb1);
+      __builtin_amdgcn_sched_barrier(0);
+      valu(Ia0, Ia1, Sa0, Sa1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(blk + 1, Ia0, Ia1, Sa0, Sa1);
+      __builtin_amdgcn_sched_barrier(0);
+      valu(Ib0, Ib1, Sb0, Sb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    valu(Ia0, Ia1, Sa0, Sa1);
+  } else if (M == M_MULR || M == M_MULL) {
+    // scale products on the VALU: S_i = dx(row i) * dw(lane) by one v_mul_f32 per element, dx
+    // from registers (MULR) or from an fp32 table in LDS (MULL: four 16-byte broadcast reads per
+    // block)
+    float* tab = reinterpret_cast<float*>(lds_reserve);
+    for (int i = threadIdx.x; i < 8 * 64; i += blockDim.x) tab[i] = 1.0f + (float)(in[i & 1023] & 1023) / 1024.0f;
+    __syncthreads();
+    const int half = lane >> 5;
+    float dxr[16];
+    for (int i = 0; i < 16; ++i) dxr[i] = Sr[i];
+    float dw0 = __int_as_float(in[lane + 900] & 0x3fffffff), dw1 = dw0 * 1.5f;
+    for (int blk = 0; blk < nblocks; ++blk) {
+      next_operands(blk);
+      const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
+      const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
+      dw0 += 1.0f;
+      dw1 += 1.0f;
+      if (M == M_MULL) {
+        const float* t = tab + (blk & 7) * 64 + 4 * half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = *reinterpret_cast<const float4*>(t + 8 * j);
+          dxr[4 * j] = v.x; dxr[4 * j + 1] = v.y; dxr[4 * j + 2] = v.z; dxr[4 * j + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float S0 = dxr[i] * dw0, S1 = dxr[i] * dw1;
+        acc0[i] = fmaf((float)I0[i], S0, acc0[i]);
+        acc1[i] = fmaf((float)I1[i], S1, acc1[i]);
+      }
+    }
+  } else if (M == M_2B) {
+    typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+    typedef float v32f __attribute__((ext_vector_type(32)));
+    v32f z32;
+    for (int i = 0; i < 32; ++i) z32[i] = 0.f;
+    for (int blk = 0; blk < nblocks; ++blk) {
+      next_operands(blk);
+      const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
+      const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
+      const v4h sx = __builtin_bit_cast(v4h, (v2i_){sa[0], 0});
+      const v4h sw = __builtin_bit_cast(v4h, (v2i_){hw[0], hw[1]});
+      const v32f S = __builtin_amdgcn_mfma_f32_32x32x4f16(sx, sw, z32, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc0[i] = fmaf((float)I0[i], S[i], acc0[i]);
+        acc1[i] = fmaf((float)I1[i], S[16 + i], acc1[i]);
+      }
+    }
+  } else if (M == M_X8) {
+    typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+    for (int blk = 0; blk < nblocks; ++blk) {
+      next_operands(blk);
+      const v4h sx = __builtin_bit_cast(v4h, (v2i_){sa[0], 0});
+      const v4h sw = __builtin_bit_cast(v4h, (v2i_){hw[0], hw[1]});
+      {
+        const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, izero, 0, 0, 0);
+        const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x8f16(sx, sw, fzero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
+      }
+      {
+        const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, izero, 0, 0, 0);
+        const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x8f16(sw, sx, fzero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
       }
     }
   } else if (M == M_PIPE) {
@@ -293,6 +431,71 @@ __global__ __launch_bounds__(256, W) void mix_kernel(const int* __restrict__ in,
   if (lds_reserve[0] == 12345) o[0] = 0.f;  // keeps the reservation
 }
 
+
+// The 2-block f16 MFMA's lane layout, checked on the host: lane l supplies A = (ax[l], 0, 0, 0),
+// B = (by[l], 0, 0, 0); D (32 registers x 64 lanes) is copied out.
+__global__ void layout_kernel(float* out) {
+  typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+  typedef float v32f __attribute__((ext_vector_type(32)));
+  const int l = threadIdx.x;
+  const v4h A = {(_Float16)(1 + l), (_Float16)0, (_Float16)0, (_Float16)0};
+  const v4h B = {(_Float16)(1.0f / 64 * (1 + (l * 7) % 64)), (_Float16)0, (_Float16)0, (_Float16)0};
+  v32f z;
+  for (int i = 0; i < 32; ++i) z[i] = 0.f;
+  const v32f D = __builtin_amdgcn_mfma_f32_32x32x4f16(A, B, z, 0, 0, 0);
+  for (int i = 0; i < 32; ++i) out[i * 64 + l] = D[i];
+}
+void layout_check(const int*, float* dout) {
+  layout_kernel<<<1, 64>>>(dout);
+  float h[2048];
+  if (hipMemcpy(h, dout, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) { printf("copy failed\n"); return; }
+  // hypothesis: register i of lane l, block k = i / 16, holds row 8 ((i % 16) / 4) + 4 (l / 32) + i % 4
+  // of block k (A from lane 32 k + row) times column l % 32 (B from lane 32 k + col)
+  int bad = 0;
+  for (int i = 0; i < 32; ++i)
+    for (int l = 0; l < 64; ++l) {
+      const int k = i / 16, ii = i % 16;
+      const int row = 8 * (ii / 4) + 4 * (l / 32) + ii % 4, col = l % 32;
+      const int la = 32 * k + row, lb = 32 * k + col;
+      const float want = (float)(1 + la) * (float)(_Float16)(1.0f / 64 * (1 + (lb * 7) % 64));
+      if (h[i * 64 + l] != want) { if (bad < 5) printf("layout: D[%d] lane %d = %g, want %g\n", i, l, h[i * 64 + l], want); ++bad; }
+    }
+  printf("2b f16 layout hypothesis: %d mismatches of 2048\n", bad);
+}
+
+
+// v_mfma_f32_32x32x8_f16's lane layout: lane l supplies A = a[l] * (1, 2, 4, 8) (rows l % 32,
+// k = 4 (l / 32) + j) and B = b[l] * (1, 1/2, 1/4, 1/8); D (16 registers x 64 lanes) copied out.
+__global__ void layout_x8_kernel(float* out) {
+  typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+  const int l = threadIdx.x;
+  const float av = (float)(1 + l), bv = 1.0f / 64 * (1 + (l * 7) % 64);
+  const v4h A = {(_Float16)av, (_Float16)(2 * av), (_Float16)(4 * av), (_Float16)(8 * av)};
+  const v4h B = {(_Float16)bv, (_Float16)(bv / 2), (_Float16)(bv / 4), (_Float16)(bv / 8)};
+  const v16f D = __builtin_amdgcn_mfma_f32_32x32x8f16(A, B, (v16f){0.f}, 0, 0, 0);
+  for (int i = 0; i < 16; ++i) out[i * 64 + l] = D[i];
+}
+void layout_check_x8(float* dout) {
+  layout_x8_kernel<<<1, 64>>>(dout);
+  float h[1024];
+  if (hipMemcpy(h, dout, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) { printf("copy failed\n"); return; }
+  // hypothesis: D[i] of lane l = row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32, and
+  // the K-sum runs over both lane halves: k = 4 h + j comes from lane 32 h + row (A), 32 h + col (B)
+  int bad = 0;
+  for (int i = 0; i < 16; ++i)
+    for (int l = 0; l < 64; ++l) {
+      const int row = 8 * (i / 4) + 4 * (l / 32) + i % 4, col = l % 32;
+      double want = 0;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int la = 32 * hh + row, lb = 32 * hh + col;
+        const double av = 1 + la, bv = (double)(float)(_Float16)(1.0f / 64 * (1 + (lb * 7) % 64));
+        for (int j = 0; j < 4; ++j) want += (double)(float)(_Float16)(av * (1 << j)) * (double)(float)(_Float16)(bv / (1 << j));
+      }
+      if ((double)h[i * 64 + l] != want) { if (bad < 5) printf("x8 layout: D[%d] lane %d = %g, want %g\n", i, l, h[i * 64 + l], want); ++bad; }
+    }
+  printf("32x32x8 f16 layout hypothesis: %d mismatches of 1024\n", bad);
+}
+
 // ns per wave-block per SIMD
 template <int M, int W>
 double mix1(int ncu, const int* din, float* dout) {
@@ -348,6 +551,12 @@ int main() {
   printf("| v_mfma_i32_16x16x64_i8 | %.2f | %.0f |\n", ns, t);
   ns = rate<R_F16_16>(ncu, din, dout, 16.0 * 16 * 32, 8, &t);
   printf("| v_mfma_f32_16x16x32_f16 | %.2f | %.0f |\n", ns, t);
+  ns = rate<R_F16_2B>(ncu, din, dout, 2.0 * 32 * 32 * 4, 4, &t);
+  printf("| v_mfma_f32_32x32x4_2b_f16 | %.2f | %.0f |\n", ns, t);
+  ns = rate<R_F16_X8>(ncu, din, dout, 32.0 * 32 * 8, 4, &t);
+  printf("| v_mfma_f32_32x32x8_f16 | %.2f | %.0f |\n", ns, t);
+  ns = rate<R_F32_2B>(ncu, din, dout, 2.0 * 32 * 32 * 1, 4, &t);
+  printf("| v_mfma_f32_32x32x1_2b_f32 | %.2f | %.0f |\n", ns, t);
   printf("\nThe MMQ's per-block mix, ns per wave-block per SIMD, at 2 / 3 / 4 wavefronts per "
          "SIMD:\n\n");
   printf("| mix | 2 | 3 | 4 |\n|---|---:|---:|---:|\n");
@@ -361,6 +570,13 @@ int main() {
   mix_row<M_PIPE>(ncu, din, dout);
   mix_row<M_AGPR>(ncu, din, dout);
   mix_row<M_VS>(ncu, din, dout);
+  mix_row<M_DEEP>(ncu, din, dout);
+  mix_row<M_MULR>(ncu, din, dout);
+  mix_row<M_MULL>(ncu, din, dout);
+  mix_row<M_2B>(ncu, din, dout);
+  mix_row<M_X8>(ncu, din, dout);
+  layout_check_x8(dout);
+  layout_check(din, dout);
   const hipError_t e = hipDeviceSynchronize();
   printf("\nstatus %s\n", hipGetErrorString(e));
   return e == hipSuccess ? 0 : 1;
