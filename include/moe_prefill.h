@@ -288,8 +288,9 @@ typedef struct moe_walk moe_walk;
 /* Creates the walk's state for a caller-owned device ring of n_slots (>= 1) slots, slot_stride
  * bytes apart (a multiple of 256): a copy stream (default priority), MOE_WALK_EVENTS + 2 events,
  * a pinned host buffer for the routing read-back, and the slot map (every slot free).  The ring
- * must stay allocated until moe_walk_destroy has returned.  *walk is set on MOE_OK; MOE_EHIP if
- * a HIP resource (or the host memory) could not be made.  A walk serves one call at a time: its
+ * must stay allocated until moe_walk_destroy has returned.  *walk is set on MOE_OK; MOE_ENOMEM if
+ * the host memory for the walk's state could not be obtained, MOE_EHIP if a HIP resource (the
+ * stream, an event, the pinned buffer) could not be made.  A walk serves one call at a time: its
  * host-side plan, read-back buffer and slot map are not guarded, so two threads must not call
  * moe_prefill_layer_streamed on the same walk at once.  For calls in sequence, even on different
  * streams, the walk's events order the reuse of its ring slots; a workspace or output shared

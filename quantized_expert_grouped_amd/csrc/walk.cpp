@@ -221,11 +221,16 @@ int moe_walk_create(void* ring, int n_slots, size_t slot_stride, moe_walk** walk
       (uintptr_t)ring % 256 != 0)
     return MOE_EINVAL;
   moe_walk* w = new (std::nothrow) moe_walk;
-  if (!w) return MOE_EHIP;
+  if (!w) return MOE_ENOMEM;
   w->ring = static_cast<uint8_t*>(ring);
   w->n_slots = n_slots;
   w->stride = slot_stride;
-  w->used_of.assign(n_slots, -1);
+  try {  // host memory: no exception crosses the C boundary
+    w->used_of.assign(n_slots, -1);
+  } catch (...) {
+    release(w);
+    return MOE_ENOMEM;
+  }
   bool ok = hipStreamCreateWithFlags(&w->copy, hipStreamNonBlocking) == hipSuccess;
   for (int i = 0; ok && i < kEvents; ++i)
     ok = hipEventCreateWithFlags(&w->used[i], hipEventDisableTiming) == hipSuccess;
@@ -446,15 +451,17 @@ static int layer_streamed(moe_walk* walk, const float* x, int T, int H, int F, i
 
   const uint8_t* arena = static_cast<const uint8_t*>(host_arena);
   // the host's experts: the MMQs skip their tiles; the pool computes their rows meanwhile
-  struct PoolJoin {  // the pool's jobs read the arena and the staging buffers: join on any exit
+  std::vector<int> stage_first(n_host + 1, 0);  // the expert's first staged row
+  std::atomic<bool> host_failed{false};
+  std::chrono::steady_clock::time_point host_t0;
+  // The pool's jobs read the arena, the staging buffers and the locals above: on any exit the
+  // pool is joined first (this object is destroyed before everything declared earlier).
+  struct PoolJoin {
     CpuPool* pool = nullptr;
     ~PoolJoin() {
       if (pool) pool->wait();
     }
   } join;
-  std::vector<int> stage_first(n_host + 1, 0);  // the expert's first staged row
-  std::atomic<bool> host_failed{false};
-  std::chrono::steady_clock::time_point host_t0;
   if (hs) {
     for (int e = 0; e < E; ++e) hs->h_skip[e] = w.streamed[e] == kHost ? 1 : 0;
     if (!ok(hipMemcpyAsync(hs->d_skip, hs->h_skip, (size_t)E, hipMemcpyHostToDevice, s)) ||
