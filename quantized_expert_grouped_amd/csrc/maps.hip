@@ -153,17 +153,28 @@ __global__ __launch_bounds__(kScanThreads) void maps_scan_kernel(
   const int nt = block_exclusive_scan(s_til, E, s_wsum);
   for (int j = tid; j < E; j += kScanThreads) {
     const int e = (ring_start + j) % E;
-    const int c = s_cnt[e];
-    if (c == 0) continue;
-    order[s_act[j]] = e;
-    if (tiles == nullptr) continue;
-    for (int m = 0; m * tile_rows < c; ++m) {
+    if (s_cnt[e] > 0) order[s_act[j]] = e;
+  }
+  // The m-tile list, every thread taking tiles t, t + 1024, ...: tile t belongs to the last ring
+  // position j whose first tile s_til[j] is at most t (positions without rows own no tile and
+  // share their successor's s_til, so that j holds rows).  One expert can own thousands of tiles
+  // (skewed routing), so the tiles are spread over the threads rather than the experts.
+  if (tiles != nullptr) {
+    for (int t = tid; t < nt; t += kScanThreads) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_til[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      const int e = (ring_start + lo) % E;
+      const int m = t - s_til[lo];
       MTile tl;
-      tl.ordinal = s_act[j];
+      tl.ordinal = s_act[lo];
       tl.expert = e;
       tl.row0 = s_off[e] + m * tile_rows;
-      tl.nrows = min(tile_rows, c - m * tile_rows);
-      tiles[s_til[j] + m] = tl;
+      tl.nrows = min(tile_rows, s_cnt[e] - m * tile_rows);
+      tiles[t] = tl;
     }
   }
   if (tid == 0) {
