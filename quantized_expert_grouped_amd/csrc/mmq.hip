@@ -329,10 +329,9 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
     const v4i hw0 = b_header<WT>(brow0);
     const v4i hw1 = b_header<WT>(brow1);
     if (WT == 1) {
-      // sum over the stage's blocks of sx_b * mw_b (added first: its operands die before the
-      // block loop): (s_0, s_1, s_2, s_3) against
-      // (m_0, m_1, m_2, m_3), both gathered from the headers' high halves; zeros in lane half 1
-      // of the fp32-output kernel
+      // sum over the stage's blocks of sx_b * mw_b, added first so that its operands die before
+      // the block loop: (s_0, s_1, s_2, s_3) against (m_0, m_1, m_2, m_3), both gathered from
+      // the headers' high halves; zeros in lane half 1 of the fp32-output kernel
       const v4h ss = __builtin_bit_cast(
           v4h, (v2i){(int)__builtin_amdgcn_perm((uint32_t)hx[1], (uint32_t)hx[0], sel_s),
                      (int)__builtin_amdgcn_perm((uint32_t)hx[3], (uint32_t)hx[2], sel_s)});
