@@ -29,6 +29,39 @@ def test_route_topk(orc, T, E, K, zipf):
     assert np.max(np.abs(gw.astype(np.float64) - ow) / ow) <= 1e-6
 
 
+def test_route_topk_signed_zeros_and_extremes(orc):
+    """Logits the order-preserving integer keys must rank as floats compare: -0.0 and +0.0 equal
+    (the lower id first), negative values only, subnormals, values near the float range's ends,
+    and a zero of either sign at the K-th place."""
+    E, K = 64, 8
+    L = np.full((6, E), -1.0, np.float32)
+    for i, z in ((5, -0.0), (3, 0.0), (10, -0.0), (2, -0.0), (40, 0.0)):
+        L[0, i] = z                                   # five zeros, mixed signs: ids 2, 3, 5, 10, 40
+    L[1] = -np.logspace(-30, 30, E).astype(np.float32)[np.random.default_rng(1).permutation(E)]
+    L[2, :] = np.float32(0.0)
+    L[2, ::3] = np.float32(1e-40)                     # subnormal positives
+    L[2, 1::3] = np.float32(-1e-40)                   # subnormal negatives
+    L[2, 7] = np.float32(-0.0)
+    L[3, :] = np.float32(-3e38)
+    L[3, [9, 4, 60, 33]] = np.float32(3e38)           # ties at the top of the range
+    L[4] = np.random.default_rng(4).standard_normal(E).astype(np.float32)
+    L[5, :] = np.float32(-2.0)
+    L[5, :7] = np.float32(1.0)
+    L[5, 20] = np.float32(-0.0)                       # the 8th pick: a zero among the -2s
+    L[5, 12] = np.float32(0.0)
+    note("route signed zeros and extremes")
+    idx = empty((6, K), torch.int32)
+    w = empty((6, K), torch.float32)
+    abi.route_topk(dev(L), K, idx, w)
+    gi, gw = host(idx), host(w)
+    oi, ow = orc.route_topk(L, K)
+    assert np.array_equal(gi, oi)
+    assert gi[0, :5].tolist() == [2, 3, 5, 10, 40]
+    assert gi[5, 7] == 12
+    # token 3's last four weights underflow to exactly 0 on both sides
+    assert np.all(np.abs(gw.astype(np.float64) - ow) <= 1e-6 * np.abs(ow))
+
+
 @pytest.mark.parametrize("T,K,E,ring", [(7, 2, 16, 0), (7, 2, 16, 9), (1, 1, 1, 0),
                                         (1000, 10, 512, 123), (8192, 10, 512, 5),
                                         (4099, 3, 2048, 2047), (513, 8, 64, 17)])
