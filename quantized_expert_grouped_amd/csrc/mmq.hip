@@ -529,13 +529,14 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   am = fmaxf(am, __shfl_xor(am, 32));
   const bool nz = am > 0.0f;
   const float d = am / 127.0f;
+  int q[16];
+  q8_round16(v, d, nz, q);
   uint32_t qw[4] = {0, 0, 0, 0};
   int S = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int q = nz ? (int)roundf(v[k] / d) : 0;
-    S += q;
-    qw[k >> 2] |= (uint32_t)(q & 0xff) << (8 * (k & 3));
+    S += q[k];
+    qw[k >> 2] |= (uint32_t)(q[k] & 0xff) << (8 * (k & 3));
   }
   S += __shfl_xor(S, 32);
   const int row = 32 * wr + rr;

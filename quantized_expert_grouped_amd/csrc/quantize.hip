@@ -4,9 +4,10 @@
 // quantises each token once and writes the same block to every row slot[t*K+k].
 //
 // Block arithmetic (identical in both forms): amax = max|v|; d = amax/127 (IEEE division);
-// q = roundf(v/d) (IEEE division, ties away from zero); S = sum q; stored d16 = fp16(d),
-// s16 = fp16(d * S); an all-zero block stores zeros.  Row layout (DS4): 144 B per 128 values =
-// 4 x (d16, s16) then 4 x 32 q.  The D4 layout, which the page names for Q8_0, keeps the 4
+// q = roundf(v/d) (the IEEE quotient, ties away from zero: taken through a reciprocal, with the
+// division itself only near half-integers, which gives the same q); S = sum q; stored
+// d16 = fp16(d), s16 = fp16(d * S); an all-zero block stores zeros.  Row layout (DS4): 144 B per
+// 128 values = 4 x (d16, s16) then 4 x 32 q.  The D4 layout, which the page names for Q8_0, keeps the 4
 // blocks' fp32 d in the same 16 header bytes instead (the same q, no s).
 //
 // A route whose expert id was out of range has slot = -1 (and its row src = -1, see the maps):
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
   // The row is taken in chunks of 1024 values (16 per lane), two chunks' loads in flight at a
   // time so that the second chunk's latency overlaps the first's quantisation and stores.
-  auto load = [&](int c0, float* v) {
+  auto load = [&](int c0, float (&v)[16]) {
     const int v0 = c0 + lane * 16;
     if (v0 < H) {  // H is a multiple of 128: whole 8-lane groups
       const float4* p = reinterpret_cast<const float4*>(xr + v0);
@@ -64,13 +65,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       for (int i = 0; i < 16; ++i) v[i] = 0.0f;
     }
   };
-  auto quantize_chunk = [&](int c0, const float* v) {
+  auto quantize_chunk = [&](int c0, const float (&v)[16]) {
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
     am = fmaxf(am, __shfl_xor(am, 1));
     const bool nz = am > 0.0f;
     const float d = am / 127.0f;
+    int q[16];
+    q8_round16(v, d, nz, q);
     int S = 0;
     uint32_t qw[4];
 #pragma unroll
@@ -78,9 +81,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       uint32_t packed = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int q = nz ? (int)roundf(v[4 * i + b] / d) : 0;
-        S += q;
-        packed |= (uint32_t)(q & 0xff) << (8 * b);
+        S += q[4 * i + b];
+        packed |= (uint32_t)(q[4 * i + b] & 0xff) << (8 * b);
       }
       qw[i] = packed;
     }

@@ -53,6 +53,59 @@ def test_quantize_d4_both_modes_bit_exact(orc, T, H, K, E):
     assert np.array_equal(g1, want)
 
 
+def _near_half_integer_rows(T: int, H: int, seed: int) -> np.ndarray:
+    """Rows whose blocks put v / d on, or within a few ulps of, a half-integer (d = amax / 127 is
+    known in advance: each block holds its amax).  Block kinds: d a power of two (exact ties);
+    (j + 0.5) d moved by 0..4096 ulps; and, on every third token, values 1e-4..3e-4 away from a
+    half-integer (close, yet outside the band where the reciprocal product is not trusted), so
+    that whole wavefronts take the fast rounding near its edge."""
+    rng = np.random.default_rng(seed)
+    nb = H // 32
+    x = np.empty((T, nb, 32), np.float32)
+    ulps = np.array([0, 1, -1, 2, -2, 3, -3, 4, -4, 6, -6, 8, -8, 16, -16, 64, -64, 256, -256,
+                     1024, -1024, 4096, -4096], np.int32)
+    for t in range(T):
+        for b in range(nb):
+            tie = t % 3 != 2 and (t * nb + b) % 8 == 0
+            am = np.float32(127.0 * 2.0 ** int(rng.integers(-20, 4)) if tie
+                            else rng.uniform(0.01, 100.0))
+            d = am / np.float32(127.0)
+            j = rng.integers(-127, 127, 31).astype(np.float64)
+            if t % 3 == 2:
+                delta = rng.uniform(1e-4, 3e-4, 31) * rng.choice([-1.0, 1.0], 31)
+                v = ((j + 0.5 + delta) * np.float64(d)).astype(np.float32)
+            else:
+                v = (j + 0.5).astype(np.float32) * d
+                if not tie:
+                    v = (v.view(np.int32) + ulps[rng.integers(0, len(ulps), 31)]).view(np.float32)
+            x[t, b, 0] = am if rng.integers(0, 2) else -am
+            x[t, b, 1:] = v
+            x[t, b] = x[t, b, rng.permutation(32)]
+    return x.reshape(T, H)
+
+
+def test_quantize_near_half_integer_quotients(orc):
+    """q = roundf(v / d) where v / d sits on or next to a half-integer (a reciprocal product alone
+    rounds thousands of these values the other way), exact ties (away from zero), and scales
+    near the bottom of the float range (d = 2^-125, the smallest taken through the reciprocal;
+    d = 2^-126 and subnormal d, which are not): both forms and both layouts against the
+    oracle's bytes."""
+    T, H, K, E = 48, 1024, 2, 16
+    x = _near_half_integer_rows(T, H, seed=77)
+    x[4, :32] *= np.float32(2.0 ** -125) * np.float32(127.0) / np.max(np.abs(x[4, :32]))
+    x[4, 32:64] *= np.float32(2.0 ** -126) * np.float32(127.0) / np.max(np.abs(x[4, 32:64]))
+    x[4, 64:96] *= np.float32(1e-37) / np.max(np.abs(x[4, 64:96]))     # d subnormal
+    x[4, 96:128] *= np.float32(3e-39) / np.max(np.abs(x[4, 96:128]))   # amax subnormal
+    rng = np.random.default_rng(78)
+    idx, _ = orc.route_topk(rng.standard_normal((T, E)).astype(np.float32), K)
+    m = orc.build_maps(idx, E)
+    for layout, flag in ((orc.DS4, 0), (orc.D4, abi.QUANT_D4)):
+        want = orc.quantize_scatter(x, K, m["slot"], layout)
+        for form in (0, abi.QUANT_PER_ROW):
+            note(f"quantize near half-integers layout={layout} form={form}")
+            assert np.array_equal(gpu_quantize(x, K, m["slot"], m["src"], flag | form), want)
+
+
 def test_quantize_full_t32k_sampled(orc):
     """T = 32768, H = 2048, K = 10 (input larger than the on-chip cache): the whole buffer in both
     modes is compared byte for byte with the oracle on 512 sampled tokens' rows, and the two modes
