@@ -90,15 +90,15 @@ struct alignas(16) StageBuf {
 // LDS stage buffers per workgroup: two (19.5 KB for Q4_1, 26.6 KB for Q8_0; one stage in flight
 // ahead of the MFMAs), so that three workgroups fit in a CU's 160 KB and in 168 VGPRs: three
 // wavefronts per SIMD hide each other's waits better than deeper prefetch does (a ring of four,
-// or three, at two workgroups per CU was 5-9% slower).  Q4_1's gate/up kernel runs four (its
-// ring fits four times in LDS, and it fits 128 VGPRs when each column tile's MFMAs and
-// convert + fma run in turn; measured 3% faster at T = 8,192); Q4_1's down kernel does not fit
-// 128 VGPRs without spills and stays at three.  The raw block-dot epilogue and the per-group
+// or three, at two workgroups per CU was 5-9% slower).  Q4_1's kernels run four (their ring
+// fits four times in LDS): gate/up fits 128 VGPRs when each column tile's MFMAs and
+// convert + fma run in turn (measured 3% faster at T = 8,192), down when each wavefront takes
+// one column tile of both row tiles (below).  The raw block-dot epilogue and the per-group
 // kernel stay at two workgroups per CU (they would spill at three).
 constexpr int kWgPerCu = 3;
 template <int WT, int EPI>
 constexpr int wg_per_cu() {
-  return EPI == 2 ? 2 : (WT == 1 && EPI == 1 ? 4 : kWgPerCu);
+  return EPI == 2 ? 2 : (WT == 1 ? 4 : kWgPerCu);
 }
 
 // The fp32-output (down) kernel's workgroup sweeps up to kSweep consecutive n-tiles of its m-tile
@@ -248,10 +248,19 @@ __device__ __forceinline__ v4i b_header(const uint8_t* brow) {
   return (v4i){(int)d.x, (int)d.y, 0, 0};
 }
 
-template <int WT, int EPI, int NG = 4>
+// Wavefront roles.  By default wavefront w computes row tile w / 2 against two column tiles.
+// Q4_1's fp32-output (down) kernel instead gives wavefront w column tile w of both row tiles:
+// each weight fragment's nibbles are then split once per workgroup instead of twice (six VALU
+// instructions per tile and block), and the kernel fits 128 VGPRs, so four workgroups share a
+// CU (measured down -9.5% at T = 8,192, -6.8% on the Zipf workload; outputs bit-identical).  The
+// SwiGLU kernel keeps the default: it needs gate and up of one feature in one wavefront.  NG
+// and NG1 are the live 8-row groups of the wavefront's (first) and second row tile; NG1 = 0
+// means row tile 1 holds none of the expert's rows.
+template <int WT, int EPI, int NG = 4, int NG1 = 4>
 __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
                                          const MmqProblem& p, const uint8_t* W, int row0,
                                          int nrows, int ntile, int nsweep = 1) {
+  constexpr bool kByColumn = WT == 1 && EPI == 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
@@ -262,7 +271,7 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   // the wavefront's two column tiles (32 LDS weight rows each)
   const int ct0 = EPI == 1 ? wc : 2 * wc;
   const int ct1 = EPI == 1 ? 2 + wc : 2 * wc + 1;
-  const bool live = 32 * wr < nrows;  // a row tile past the expert's rows does no math
+  const bool live = kByColumn || 32 * wr < nrows;  // a row tile past the expert's rows: no math
   const int nstages = p.k_in / kDs4Vals;
   const uint8_t* abase = p.act + (size_t)row0 * act_row_bytes;
 
@@ -321,6 +330,56 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
             out[(r * p.n_out + n0 + 32 * ct1 + l32) * nblk + kb] = I1[i];
           }
         }
+      }
+      return;
+    }
+    if (kByColumn) {  // column tile `wave` of row tiles 0 and 1
+      const uint8_t* arow0 = cur.a + l32 * kARow;
+      const uint8_t* arow1 = cur.a + (32 + l32) * kARow;
+      const uint8_t* brow = cur.b + (32 * wave + l32) * Geo<WT>::kBRow;
+      const v4i hx0 = *reinterpret_cast<const v4i*>(arow0);
+      const v4i hw = b_header<WT>(brow);
+      // the min term as in the default roles, for each row tile
+      const v4h m = __builtin_bit_cast(
+          v4h, (v2i){(int)__builtin_amdgcn_perm((uint32_t)hw[1], (uint32_t)hw[0], 0x07060302u),
+                     (int)__builtin_amdgcn_perm((uint32_t)hw[3], (uint32_t)hw[2], 0x07060302u)});
+      const v4h ss0 = __builtin_bit_cast(
+          v4h, (v2i){(int)__builtin_amdgcn_perm((uint32_t)hx0[1], (uint32_t)hx0[0], sel_s),
+                     (int)__builtin_amdgcn_perm((uint32_t)hx0[3], (uint32_t)hx0[2], sel_s)});
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(ss0, m, acc0, 0, 0, 0);
+      v4i hx1 = hx0;
+      if (NG1 > 0) {
+        hx1 = *reinterpret_cast<const v4i*>(arow1);
+        const v4h ss1 = __builtin_bit_cast(
+            v4h, (v2i){(int)__builtin_amdgcn_perm((uint32_t)hx1[1], (uint32_t)hx1[0], sel_s),
+                       (int)__builtin_amdgcn_perm((uint32_t)hx1[3], (uint32_t)hx1[2], sel_s)});
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(ss1, m, acc1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < kKB; ++b) {
+        const v4i xb = b_unpack<WT>(b_raw<WT>(brow, b, half));  // split once, used twice
+        const v4h w =
+            __builtin_bit_cast(v4h, (b >> 1) ? (v2i){hw[2], hw[3]} : (v2i){hw[0], hw[1]});
+        {
+          const uint32_t sv = (uint32_t)hx0[b] & keep_lo;
+          const v4h sx = __builtin_bit_cast(v4h, (b & 1) ? (v2i){0, (int)sv} : (v2i){(int)sv, 0});
+          const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_frag<WT>(arow0, b, half), xb,
+                                                                izero, 0, 0, 0);
+          const v16f S0 = __builtin_amdgcn_mfma_f32_32x32x8f16(sx, w, fzero, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4 * NG; ++i) acc0[i] = fmaf((float)I0[i], S0[i], acc0[i]);
+        }
+        if (NG1 > 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          const uint32_t sv = (uint32_t)hx1[b] & keep_lo;
+          const v4h sx = __builtin_bit_cast(v4h, (b & 1) ? (v2i){0, (int)sv} : (v2i){(int)sv, 0});
+          const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_frag<WT>(arow1, b, half), xb,
+                                                                izero, 0, 0, 0);
+          const v16f S1 = __builtin_amdgcn_mfma_f32_32x32x8f16(sx, w, fzero, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4 * NG1; ++i) acc1[i] = fmaf((float)I1[i], S1[i], acc1[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       return;
     }
@@ -428,6 +487,22 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   // lies 32 floats after ct0.
   auto store_f32 = [&](int j) {
     const int wu = wave_id();  // wr and ct0 as scalars
+    if (kByColumn) {  // column tile wu of row tiles 0 and 1 (32 rows further down)
+      const char* ob = reinterpret_cast<const char*>(p.out) +
+                       ((size_t)row0 * p.n_out + n0 + j * kRowsN + 32 * wu) * 4;
+      const uint32_t off = (uint32_t)((4 * half * p.n_out + l32) * 4);
+      const size_t tile1 = (size_t)32 * p.n_out * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+        const char* rb = ob + (size_t)(8 * (i >> 2) + (i & 3)) * p.n_out * 4 + off;
+        if (row < nrows) *(float*)rb = acc0[i];
+        if (NG1 > 0 && 32 + row < nrows) *(float*)(rb + tile1) = acc1[i];
+        acc0[i] = 0.0f;
+        acc1[i] = 0.0f;
+      }
+      return;
+    }
     const char* ob =
         reinterpret_cast<const char*>(p.out) +
         ((size_t)(row0 + 32 * (wu >> 1)) * p.n_out + n0 + j * kRowsN + 64 * (wu & 1)) * 4;
@@ -598,6 +673,26 @@ __global__ __launch_bounds__(256, (wg_per_cu<WT, EPI>())) void mmq_layer_kernel(
   // EPI 0: the workgroup's n-tiles kSweep * (work % ntl) onwards, at most kSweep of them
   const int nt0 = EPI == 0 ? (work % ntl) * kSweep : work % ntl;
   const int nsw = EPI == 0 ? min(kSweep, p.n_out / kRowsN - nt0) : 1;
+  if (WT == 1 && EPI == 0) {  // by column: the live 8-row groups of both row tiles
+    const int nr = t.nrows;
+    if (nr > 56)
+      mmq_tile<WT, EPI, 4, 4>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    else if (nr > 48)
+      mmq_tile<WT, EPI, 4, 3>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    else if (nr > 40)
+      mmq_tile<WT, EPI, 4, 2>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    else if (nr > 32)
+      mmq_tile<WT, EPI, 4, 1>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    else if (nr > 24)
+      mmq_tile<WT, EPI, 4, 0>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    else if (nr > 16)
+      mmq_tile<WT, EPI, 3, 0>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    else if (nr > 8)
+      mmq_tile<WT, EPI, 2, 0>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    else
+      mmq_tile<WT, EPI, 1, 0>(ring.buf[0], ring.buf[1], p, W, t.row0, nr, nt0, nsw);
+    return;
+  }
   if (ng == 4)
     mmq_tile<WT, EPI, 4>(ring.buf[0], ring.buf[1], p, W, t.row0, t.nrows, nt0, nsw);
   else if (ng == 3)
