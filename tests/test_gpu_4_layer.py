@@ -136,6 +136,39 @@ def test_layer_edge_cases(orc, edge):
     assert rel_err(got, want) <= TOL
 
 
+# Rows per expert that put an expert's last 64-row tile in every case the MMQ launches treat
+# apart: each count of live 8-row groups in the first and the second 32-row tile, whole tiles,
+# and one row past them; the last four experts receive no rows.
+TILE_ROWS = [1, 7, 8, 9, 16, 17, 24, 25, 31, 32, 33, 40, 41, 48, 49, 56, 57, 63, 64, 65, 96, 127,
+             128, 129, 0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_1, synth.Q8_0])
+def test_layer_tile_row_counts(orc, wtype):
+    """Experts with exactly the row counts above (one expert per token, K = 1), so that every
+    partial-tile form of both MMQ launches runs: output and the down projection's rows against
+    the oracle."""
+    counts = np.array(TILE_ROWS)
+    E, T, H, F = len(counts), int(counts.sum()), 256, 256
+    c = synth.make_case("tile_rows", T=T, H=H, F=F, E=E, K=1, wtype=wtype, seed=77 + wtype)
+    rng = np.random.default_rng(5 + wtype)
+    idx = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, 1)
+    w = np.ones((T, 1), np.float32)
+    want, dbg = orc.prefill_layer(c.x, idx, w, wtype, c.pool, c.expert_off, F, E, debug=True)
+    layer = _layer(c)
+    got = _run(layer, c, idx, w)
+    assert rel_err(got, want) <= TOL
+    ws = host(layer.ws)
+    o = abi.workspace_offset(abi.WS_DM, T, H, F, E, 1, wtype, 16)
+    Dm = ws[o:o + T * H * 4].view(np.float32).reshape(T, H)
+    m = orc.build_maps(idx, E, c.ring_start)
+    assert np.array_equal(np.bincount(idx[:, 0], minlength=E), m["counts"])
+    for e in range(E):                       # every expert's rows, each within the bound
+        r0, r1 = m["offsets"][e], m["offsets"][e + 1]
+        if r1 > r0:
+            assert rel_err(Dm[r0:r1], dbg["Dm"][r0:r1]) <= TOL, (e, r1 - r0)
+
+
 def test_layer_step_with_gpu_routing(orc):
     """Routing and the layer in one pass on the GPU (the benchmark's step)."""
     c = synth.make_case("step", T=300, H=512, F=256, E=32, K=4, wtype=synth.Q4_1, seed=8)
