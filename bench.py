@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -95,11 +96,19 @@ STAGE_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """A kernel source without its comments and with its whitespace collapsed, so that a change
+    to comments alone keeps the hash (the compiled code is the same)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def stage_source_hash(stage: str) -> str:
     h = hashlib.sha256()
     for f in STAGE_SOURCES[stage]:
-        with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

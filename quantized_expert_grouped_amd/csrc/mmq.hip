@@ -483,11 +483,10 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   // EPI 0: n-tile j's fp32 rows, then the accumulators cleared for the next n-tile.  The rows are
   // stored non-temporally, as nothing reads them before the combine, after the whole launch
   // (measured: down -0.5% / -1.1% and the combine that reads them -6% at T = 8,192 / 32,768).
-  // Register i
-  // holds row 32 wr + 8 (i / 4) + 4 half + i % 4: its address is a wavefront-uniform row base
-  // (scalar arithmetic) plus one 32-bit lane offset that does not change with i (4 half rows
-  // and the lane's column; below 2^31 bytes as 64 rows x n_out floats are); column tile ct1
-  // lies 32 floats after ct0.
+  // In the default roles register i holds row 32 wr + 8 (i / 4) + 4 half + i % 4: its address
+  // is a wavefront-uniform row base (scalar arithmetic) plus one 32-bit lane offset that does
+  // not change with i (4 half rows and the lane's column; below 2^31 bytes as 64 rows x n_out
+  // floats are); column tile ct1 lies 32 floats after ct0.
   auto store_f32 = [&](int j) {
     const int wu = wave_id();  // wr and ct0 as scalars
     if (kByColumn) {  // column tile wu of row tiles 0 and 1 (32 rows further down)
