@@ -33,31 +33,52 @@ __device__ __forceinline__ uint32_t q8_1_scale_bits(float d, int S) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
-// q[k] = roundf(v[k] / d) (the IEEE quotient rounded half away from zero) for a lane's 16 values
-// of one q8_1 block, bit for bit, with one multiply per value in place of a division.  The block
-// scale is d = amax / 127, so |v / d| <= 127.00001.  y = v * rcp(d), with rcp within 1 ulp, lies
-// within |v / d| * (2^-23 + 2^-24) of v / d, and the correctly rounded quotient within half its
-// ulp (2^-18): together under 2.7e-5, or 4.3e-5 were rcp off by 2 ulp.  So wherever y is more
-// than 2^-14 away from every half-integer, the quotient lies strictly between the same two
-// half-integers as y and both round to the nearest integer of y, rint(y).  Values within 2^-14
-// of a half-integer (about one in 8,000), NaN, and a d outside rcp's exact range (a subnormal
-// d) send the wavefront through the IEEE division for all its values.  `nz` false (an all-zero
-// block, amax = 0) gives q = 0: there the multiplier is 0, so y = 0 (NaN values, which amax
-// skips, also take the division, which then gives 0).
-__device__ __forceinline__ void q8_round16(const float (&v)[16], float d, bool nz, int (&q)[16]) {
+// The q8_1 bytes of a lane's 16 values of one block: q[k] = roundf(v[k] / d) (the IEEE quotient
+// rounded half away from zero), bit for bit, packed four to a word (value 4i + j in byte j of
+// word i), and their sum S; an all-zero block (`nz` false, amax = 0) gives q = 0.  No division
+// per value: the block scale is d = amax / 127, so |v / d| <= 127.00001, and y = v * rcp(d) is
+// taken exactly inside two fma.  y + 1.5 * 2^23, rounded once, is rint(y) + 1.5 * 2^23 (|y| <
+// 2^22), whose low mantissa bits hold the integer in two's complement: its low byte is the q
+// byte, and the words' sum less 16 * 0x4B400000 is S.  y - rint(y) comes from the second fma.
+// With rcp within 1 ulp, |y - v / d| <= |v / d| * 2^-23, and the correctly rounded quotient lies
+// within half its ulp (2^-18) of v / d: under 1.9e-5 in all (3.4e-5 were rcp off by 2 ulp).  So
+// wherever y is more than 2^-14 away from every half-integer, the quotient lies strictly between
+// the same two half-integers as y and both round to rint(y).  Values within 2^-14 of a
+// half-integer (about one in 8,000), NaN, and a d outside rcp's exact range (a subnormal d) send
+// the wavefront through the IEEE division for all its values (NaN values, which amax skips,
+// then give what the division gives; with `nz` false the multiplier is 0).  The low bytes are
+// gathered by v_perm, two per instruction.
+__device__ __forceinline__ int q8_pack16(const float (&v)[16], float d, bool nz,
+                                         uint32_t (&qw)[4]) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23, bits 0x4B400000
   const float r = nz ? __builtin_amdgcn_rcpf(d) : 0.0f;
   bool near = nz && !(d >= 0x1p-125f);
+  int bits[16];
+  uint32_t sum = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const float y = v[k] * r;
-    const float n = __builtin_rintf(y);
-    near |= !(fabsf(y - n) < 0.5f - 0x1p-14f);  // y - n is exact; NaN compares false
-    q[k] = (int)n;
+    const float nm = fmaf(v[k], r, kMagic);
+    const float n = nm - kMagic;  // exact
+    near |= !(fabsf(fmaf(v[k], r, -n)) < 0.5f - 0x1p-14f);  // NaN compares false
+    bits[k] = __float_as_int(nm);
+    sum += (uint32_t)bits[k];
   }
+  int S = (int)(sum - 16u * 0x4B400000u);  // modulo 2^32: the sum of the q
   if (__builtin_expect(ballot(near) != 0, 0)) {
+    S = 0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) q[k] = nz ? (int)roundf(v[k] / d) : 0;
+    for (int k = 0; k < 16; ++k) {
+      bits[k] = nz ? (int)roundf(v[k] / d) : 0;
+      S += bits[k];
+    }
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // bytes 0, 1 from values 4i, 4i + 1; 2, 3 from 4i + 2, 4i + 3
+    const uint32_t b0 = (uint32_t)bits[4 * i], b1 = (uint32_t)bits[4 * i + 1];
+    const uint32_t b2 = (uint32_t)bits[4 * i + 2], b3 = (uint32_t)bits[4 * i + 3];
+    qw[i] = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
+  }
+  return S;
 }
 
 // Number of set bits of `mask` in lanes below this one.

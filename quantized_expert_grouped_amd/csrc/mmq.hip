@@ -18,11 +18,11 @@
 // The f16 MFMAs' K-sum runs over both lane halves.  In the fp32-output kernel the second half's
 // activation-scale operand is zero, so each product dx_b * dw_b (and mw_b * sx_b) enters once;
 // the SwiGLU kernel feeds the scale from both halves, so it gets exactly 2*S_b and 2*mw_b*sx_b,
-// and halves its accumulators once before the epilogue, which in binary floating point changes
-// no rounding (one multiply per tile instead of masks held in registers).  Blocks are taken in
-// ascending order and every output element is accumulated by one lane in one fixed instruction
-// sequence, so results do not depend on the tiling, the group size, the ring start or the row's
-// place in its tile.
+// and its epilogue takes the factor 2 out inside silu's argument and with one final quarter,
+// which in binary floating point changes no rounding (instead of masks held in registers).
+// Blocks are taken in ascending order and every output element is accumulated by one lane in
+// one fixed instruction sequence, so results do not depend on the tiling, the group size, the
+// ring start or the row's place in its tile.
 //
 // Workgroup: 64 activation rows (one m-tile of one expert) x 128 weight rows, 4 wavefronts; the
 // fp32-output kernel's workgroup goes on through up to 4 such weight-row tiles (n-tiles) in turn.
@@ -575,11 +575,6 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   if (!live) return;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {  // remove the factor 2 of the doubled scales (exact)
-    acc0[i] *= 0.5f;
-    acc1[i] *= 0.5f;
-  }
 
   // EPI == 1: h = silu(g) * u, then q8_1 along F.  A lane holds one feature of 16 rows; the
   // wavefront's 32 x 32 block of h goes through LDS so that two lanes own one row's block of 32
@@ -589,9 +584,12 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   float* xs = reinterpret_cast<float*>(&L0) + wave * 32 * 32;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float g = acc0[i], u = acc1[i];
+    // the accumulators hold 2g and 2u (the doubled scale products): the halving goes into the
+    // exponent's argument and one final quarter, each exact, so h = silu(g) * u as if halved
+    // first
+    const float g2 = acc0[i], u2 = acc1[i];
     xs[(8 * (i >> 2) + 4 * half + (i & 3)) * 32 + l32] =
-        g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+        g2 * __builtin_amdgcn_rcpf(1.0f + __expf(-0.5f * g2)) * u2 * 0.25f;
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
   const int rr = lane & 31, part = lane >> 5;  // row of the wavefront's 32, 16-feature half
@@ -607,15 +605,8 @@ __device__ __forceinline__ void mmq_tile(StageBuf<WT>& L0, StageBuf<WT>& L1,
   am = fmaxf(am, __shfl_xor(am, 32));
   const bool nz = am > 0.0f;
   const float d = am / 127.0f;
-  int q[16];
-  q8_round16(v, d, nz, q);
-  uint32_t qw[4] = {0, 0, 0, 0};
-  int S = 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    S += q[k];
-    qw[k >> 2] |= (uint32_t)(q[k] & 0xff) << (8 * (k & 3));
-  }
+  uint32_t qw[4];
+  int S = q8_pack16(v, d, nz, qw);
   S += __shfl_xor(S, 32);
   const int row = 32 * wr + rr;
   if (row < nrows) {

@@ -7,8 +7,8 @@
 // q = roundf(v/d) (the IEEE quotient, ties away from zero: taken through a reciprocal, with the
 // division itself only near half-integers, which gives the same q); S = sum q; stored
 // d16 = fp16(d), s16 = fp16(d * S); an all-zero block stores zeros.  Row layout (DS4): 144 B per
-// 128 values = 4 x (d16, s16) then 4 x 32 q.  The D4 layout, which the page names for Q8_0, keeps the 4
-// blocks' fp32 d in the same 16 header bytes instead (the same q, no s).
+// 128 values = 4 x (d16, s16) then 4 x 32 q.  The D4 layout, which the page names for Q8_0, keeps
+// the 4 blocks' fp32 d in the same 16 header bytes instead (the same q, no s).
 //
 // A route whose expert id was out of range has slot = -1 (and its row src = -1, see the maps):
 // nothing is written for it.
@@ -72,20 +72,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     am = fmaxf(am, __shfl_xor(am, 1));
     const bool nz = am > 0.0f;
     const float d = am / 127.0f;
-    int q[16];
-    q8_round16(v, d, nz, q);
-    int S = 0;
     uint32_t qw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        S += q[4 * i + b];
-        packed |= (uint32_t)(q[4 * i + b] & 0xff) << (8 * b);
-      }
-      qw[i] = packed;
-    }
+    int S = q8_pack16(v, d, nz, qw);
     S += __shfl_xor(S, 1);
     const uint32_t hdr =
         !nz ? 0u : D4 ? __float_as_uint(d) : (f2h(d) | (q8_1_scale_bits(d, S) << 16));
